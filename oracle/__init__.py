@@ -1,0 +1,128 @@
+"""Float64 CPU oracle for exact attention (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package. The HIP library never imports,
+links or calls it, and it imports nothing from the HIP library: the two share
+only the seeded input generators in ``workloads.py``.
+
+``attention`` evaluates the plain definition O = softmax(Q K^T * scale + mask) V
+row by row in double precision (the C source states each passage it follows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 1
+BF16 = 0
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain C, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Open a compiled oracle library and declare its entry point."""
+    lib = ctypes.CDLL(path)
+    f = lib.oracle_attention
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_double, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _as_input(x):
+    """Return (contiguous ndarray holding the raw element bits, dtype code)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy().view(np.uint16), BF16
+            if x.dtype == torch.float32:
+                return x.numpy(), F32
+            raise TypeError(f"oracle inputs must be float32 or bfloat16, got {x.dtype}")
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16:  # raw bfloat16 bits
+        return x, BF16
+    raise TypeError(f"oracle inputs must be float32 or raw bfloat16 (uint16), got {x.dtype}")
+
+
+def attention(q, k, v, scale: float, causal: bool = False, rows=None,
+              want_p: bool = False, threads: int | None = None):
+    """Float64 attention for q [B,H,Nq,d], k/v [B,H,Nk,d] (float32 or bfloat16).
+
+    ``rows``: optional flat row ids (b*H + h)*Nq + i to evaluate (sampled
+    checks); default all rows. ``scale`` is used as the exact double given;
+    callers pass the float32-rounded value the kernel receives.
+    Returns (o [nrows, d] float64, lse [nrows] float64[, p [nrows, Nk]]).
+    """
+    qa, dt = _as_input(q)
+    ka, dtk = _as_input(k)
+    va, dtv = _as_input(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k and v must share one dtype")
+    if qa.ndim != 4 or ka.ndim != 4 or va.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = qa.shape
+    if ka.shape[:2] != (B, H) or ka.shape[3] != d or va.shape != ka.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    Nk = ka.shape[2]
+    if rows is None:
+        rows_arr = None
+        nrows = B * H * Nq
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = int(rows_arr.size)
+    threads = threads or default_threads()
+    o = np.empty((nrows, d), np.float64)
+    lse = np.empty((nrows,), np.float64)
+    p = np.empty((nrows, Nk), np.float64) if want_p else None
+    scratch = np.empty((threads, Nk), np.float64)
+    rc = _load().oracle_attention(
+        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, B, H, Nq, Nk, d,
+        float(scale), int(bool(causal)),
+        rows_arr.ctypes.data if rows_arr is not None else None, nrows, threads,
+        scratch.ctypes.data, o.ctypes.data, lse.ctypes.data,
+        p.ctypes.data if p is not None else None)
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments")
+    return (o, lse, p) if want_p else (o, lse)

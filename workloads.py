@@ -1,0 +1,125 @@
+"""Seeded synthetic attention workloads: shapes, seeds and value distributions.
+
+This module only draws random numbers and names shapes. It holds none of the
+attention arithmetic, so both the float64 oracle and the HIP path may take
+their inputs from it.
+
+Recipe (the same for every workload): per tensor, a ``torch.Generator`` on the
+target device is seeded with ``10*c + t`` (c = workload number 1..5, t = 0 for
+Q, 1 for K, 2 for V); then, for b = 0..B-1 in order, one ``torch.randn`` call
+draws the [H, N, d] float32 slice, which is multiplied by the workload's scale
+factor and rounded to the storage dtype (bfloat16 rounding is
+round-to-nearest-even). The oracle always consumes the rounded bytes, so input
+quantisation is never counted as kernel error. Different devices give
+different (equally valid) draws for one seed; a test always reads back the
+bytes the kernel received.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    number: int
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: torch.dtype
+    causal: bool
+    qk_mult: float = 1.0   # Q and K are drawn N(0,1) and multiplied by this
+    num_splits: int = 0    # > 0: the split-KV decode path with this many chunks
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), rounded to float32 as the kernel receives it."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOPs of the two contractions: 4*B*H*Nq*Nk*d, halved if causal."""
+        f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def elem_bytes(self) -> int:
+        return torch.tensor([], dtype=self.dtype).element_size()
+
+    @property
+    def io_bytes(self) -> int:
+        """Compulsory HBM bytes: read Q, K, V once; write O (fp32) and LSE (fp32) once."""
+        e = self.elem_bytes
+        q = self.B * self.H * self.Nq * self.d * e
+        kv = 2 * self.B * self.H * self.Nk * self.d * e
+        o = self.B * self.H * self.Nq * self.d * 4
+        lse = self.B * self.H * self.Nq * 4
+        return q + kv + o + lse
+
+
+WORKLOADS = {
+    1: Workload(1, "f32 single head N=256 d=64", 1, 1, 256, 256, 64, torch.float32, False),
+    2: Workload(2, "bf16 B=4 H=16 N=2048 d=64", 4, 16, 2048, 2048, 64, torch.bfloat16, False),
+    3: Workload(3, "bf16 causal B=2 H=16 N=8192 d=128, Q,K x3", 2, 16, 8192, 8192, 128,
+                torch.bfloat16, True, qk_mult=3.0),
+    4: Workload(4, "bf16 causal B=1 H=32 N=30000 d=128", 1, 32, 30000, 30000, 128,
+                torch.bfloat16, True),
+    5: Workload(5, "bf16 decode B=16 H=32 Nk=32768 d=128, 64 splits", 16, 32, 1, 32768, 128,
+                torch.bfloat16, False, num_splits=64),
+}
+
+
+def draw(shape, seed: int, mult: float = 1.0, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
+    """Draw a [B, ...] tensor slice by slice along dim 0 (see the module recipe)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=dtype, device=device)
+    for b in range(shape[0]):
+        x = torch.randn(tuple(shape[1:]), generator=g, dtype=torch.float32, device=device)
+        if mult != 1.0:
+            x.mul_(mult)
+        out[b].copy_(x)  # float32 -> storage dtype, round-to-nearest-even
+        del x
+    return out
+
+
+def make_inputs(w: Workload, device="cpu"):
+    """(q, k, v) for workload ``w`` on ``device``, following the module recipe."""
+    c = w.number
+    q = draw((w.B, w.H, w.Nq, w.d), 10 * c + 0, w.qk_mult, w.dtype, device)
+    k = draw((w.B, w.H, w.Nk, w.d), 10 * c + 1, w.qk_mult, w.dtype, device)
+    v = draw((w.B, w.H, w.Nk, w.d), 10 * c + 2, 1.0, w.dtype, device)
+    return q, k, v
+
+
+def sample_rows(w: Workload, per_head: int = 64, seed: int = 12345):
+    """Flat row ids (b*H + h)*Nq + i for a sampled parity check on a large workload.
+
+    Per (b, h): fixed rows that straddle every power-of-two tile edge from 16
+    to 256 and the ragged tail, plus seeded random rows, ``per_head`` in total.
+    """
+    N = w.Nq
+    fixed = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,
+             N // 2, N - 129, N - 65, N - 49, N - 48, N - 47, N - 17, N - 2, N - 1]
+    fixed = sorted({i for i in fixed if 0 <= i < N})
+    g = torch.Generator().manual_seed(seed)
+    rows = []
+    for bh in range(w.B * w.H):
+        chosen = list(fixed)
+        extra = max(0, min(per_head, N) - len(chosen))
+        if extra:
+            pool = torch.randperm(N, generator=g).tolist()
+            have = set(chosen)
+            for i in pool:
+                if len(chosen) >= len(fixed) + extra:
+                    break
+                if i not in have:
+                    chosen.append(i)
+                    have.add(i)
+        rows.extend(bh * N + i for i in sorted(chosen))
+    return rows
