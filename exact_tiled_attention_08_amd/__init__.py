@@ -1,0 +1,181 @@
+"""Python binding of libfa.so: exact tiled attention on MI355X (gfx950).
+
+Argument marshalling only. Every step of the computation runs in the HIP kernels
+of libfa.so; torch tensors are used for device memory and the current stream.
+There is no CPU or PyTorch fallback: if the library is missing, or a tensor is
+not on the GPU, the call raises.
+
+    o, lse = fwd(q, k, v, scale=None, causal=False)        # prefill
+    o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
+
+Shapes are [B, H, N, d] (d innermost, contiguous); o is float32 [B, H, Nq, d],
+lse float32 [B, H, Nq]. The C header include/fa.h states the full contract.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "status_str", "library", "FaError",
+           "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
+           "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
+FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
+FA_BF16, FA_F32 = 0, 1
+
+# every symbol include/fa.h declares
+EXPORTS = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_status_str",
+           "fa_last_hip_error", "fa_last_hip_error_str")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
+    "fa_status_str": (ctypes.c_char_p, [_i]),
+    "fa_last_hip_error": (_i, []),
+    "fa_last_hip_error_str": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A status other than FA_OK from libfa.so."""
+
+    def __init__(self, status: int, what: str):
+        lib = library()
+        self.hip_error = int(lib.fa_last_hip_error())
+        hip = lib.fa_last_hip_error_str().decode()
+        super().__init__(f"{what}: {status_str(status)} (status {status}; HIP error "
+                         f"{self.hip_error}: {hip})")
+        self.status = status
+
+
+def library():
+    """The loaded libfa.so (ctypes.CDLL). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m exact_tiled_attention_08_amd.build "
+                "or __graft_entry__.build()); there is no fallback path")
+        # Load torch's HIP runtime first: libfa.so then binds to that same runtime (one
+        # libamdhip64 per process) instead of pulling in a second copy that would not share
+        # torch's device context, memory or streams.
+        import torch  # noqa: F401
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return library().fa_status_str(int(status)).decode()
+
+
+def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(library().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def _raise(status: int, what: str):
+    if status == FA_OK:
+        return
+    msg = f"{what}: {status_str(status)} (status {status})"
+    if status == FA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    if status in (FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_VALUE, FA_ERR_ALIGN, FA_ERR_WORKSPACE):
+        raise ValueError(msg)
+    raise FaError(status, what)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise NotImplementedError(f"unsupported dtype {t.dtype}: q, k, v must be bfloat16 or float32")
+
+
+def _check_inputs(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    B, H, _, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+
+
+def _stream_ptr(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+        return_lse: bool = True):
+    """Attention forward on the GPU. Returns (o, lse) (lse None if return_lse is False)."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    elif out.shape != (B, H, Nq, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, H, Nq, d] tensor")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None,
+                          B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
+                          _stream_ptr(q.device))
+    _raise(st, "fa_fwd")
+    return out, lse
+
+
+def decode(q, k, v, num_splits: int = 64, scale: float | None = None, out=None, lse=None,
+           workspace=None):
+    """Split-KV decode: q [B, H, 1, d] against k, v [B, H, Nk, d]. Returns (o, lse)."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    if Nq != 1:
+        raise ValueError("decode takes exactly one query per (b, h): q must be [B, H, 1, d]")
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, 1, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    st = library().fa_decode_splitkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, H, Nk, d, float(scale), int(num_splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _dtype_code(q), _stream_ptr(q.device))
+    _raise(st, "fa_decode_splitkv")
+    return out, lse

@@ -1,0 +1,130 @@
+// C ABI of libfa.so: argument validation, then dispatch to the HIP launchers.
+// Validation makes no HIP call, so a rejected call launches and writes nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr long long kMaxHeadElems = 1LL << 30;  // Nk * d per head: 32-bit in-head offsets
+constexpr int kMaxSplits = 1024;
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// hipError_t of the most recent failed launch on this thread (hipSuccess if none).
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+fa_status finish_launch(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = e;
+  return FA_ERR_HIP;
+}
+
+// (b, h) pairs handled together on one XCD (see fa::map_block).
+int heads_per_group(int BH) { return (BH % 8 == 0) ? BH / 8 : 1; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "a size is < 1 or the sizes overflow the index range";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or size";
+    case FA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+    case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case FA_ERR_VALUE: return "scale must be finite and > 0; causal must be 0 or 1";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+int fa_last_hip_error(void) { return (int)g_last_hip_error; }
+
+const char* fa_last_hip_error_str(void) { return hipGetErrorString(g_last_hip_error); }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX || BH * (long long)Nq * d > (1LL << 62) / 4) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+
+  const int br = dtype == FA_BF16 ? fa::fwd_bf16_block_rows(d) : fa::fwd_f32_block_rows(d);
+  const long long nqt = (Nq + br - 1) / br;
+  if (BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)BH;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.off = Nk - Nq;
+  p.nqt = (int)nqt;
+  p.hpg = heads_per_group((int)BH);
+  p.c = scale * fa::kLog2e;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, d, causal != 0, (hipStream_t)stream)
+                                  : fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream);
+  return finish_launch(e);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 1 || H < 1 || d < 1 || num_splits < 1) return 0;
+  const unsigned long long n = (unsigned long long)B * H * num_splits;
+  const unsigned long long per = (unsigned long long)(d + 2) * 4ull;
+  if (n > (1ull << 62) / per) return 0;
+  return (size_t)(n * per);
+}
+
+fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                            int B, int H, int Nk, int d, float scale, int num_splits,
+                            void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                            void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nk < 1 || d < 1 || num_splits < 1) return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH * num_splits > INT32_MAX) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_VALUE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+
+  fa::DecodeParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)BH;
+  p.Nk = Nk;
+  p.S = num_splits;
+  p.chunk = (Nk + num_splits - 1) / num_splits;
+  p.c = scale * fa::kLog2e;
+  // workspace: partial sums o [BH][S][d], then partial (m, l) [BH][S][2]
+  p.ws_o = (float*)workspace;
+  p.ws_ml = p.ws_o + (size_t)BH * num_splits * d;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  hipError_t e = fa::launch_decode(p, d, dtype == FA_BF16, (hipStream_t)stream);
+  return finish_launch(e);
+}
+
+}  // extern "C"

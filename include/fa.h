@@ -1,0 +1,122 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact tiled attention library (libfa.so).
+ *
+ * Computes exact scaled-dot-product attention
+ *
+ *     O = softmax(Q K^T * scale + mask) V,     LSE = log(sum_j exp(S_ij))
+ *
+ * tile by tile with the online-softmax recurrence (running row max m, running
+ * sum of exponentials l, rescale of the accumulated output by exp(m_old - m_new)),
+ * so the Nq x Nk score and probability matrices never reach device memory.
+ *   - The operation: "Flash Attention Optimization", section "Attention is not
+ *     slow because of arithmetic" (S = QK^T/sqrt(d), P = softmax(S), O = PV), and
+ *     "Explain FlashAttention. Why is it called IO-aware, and what does it actually
+ *     save?", section "Keep only the state needed for the final weighted average"
+ *     (scale, then mask, then softmax; running state m, l, o).
+ *   - The recurrence and why it is exact: "FlashAttention: Attention Is Limited by
+ *     Memory, Not Math", section "How tiling and online softmax stay exact".
+ *   - Split-KV decode with a merge of partial (m, l, o) states: same page, section
+ *     "Where it helps, and where it does not" (Flash-Decoding), with the two-sided
+ *     merge of "Flash Attention Optimization", section "The fix: tile the
+ *     computation, never materialize the full matrix".
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or synchronises; it launches asynchronously on
+ *     `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *   - Layout: contiguous row-major [B][H][N][d] (d innermost) for q, k, v and o;
+ *     [B][H][Nq] for lse. q, k, v and o must be 16-byte aligned.
+ *   - q, k, v hold FA_BF16 (bfloat16) or FA_F32 (IEEE float32) elements; o and
+ *     lse are always float32.
+ *   - Causal masking uses absolute positions with the query block aligned to the
+ *     END of the key sequence: query i (0-based) sits at position i + (Nk - Nq)
+ *     and sees key j iff j <= i + (Nk - Nq). For Nq == Nk this is j <= i.
+ *     ("Explain FlashAttention ...", section "Executable recurrence, with an
+ *     empty-state policy": masks use global positions, not tile-local ones.)
+ *   - A query row that sees no key (only possible when causal and Nq > Nk) gets
+ *     O = 0 and LSE = -inf (the empty-row policy of the same section).
+ *   - LSE is the natural-log log-sum-exp of the scaled, masked scores of the row.
+ *   - Arguments are validated before any HIP call; a rejected call launches
+ *     nothing and writes nothing. There is no silent fallback: unsupported
+ *     shapes return FA_ERR_UNSUPPORTED. NaN/Inf in q, k or v is outside the
+ *     contract (not scanned for).
+ *   - Stateless and thread-safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,         /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = -2,        /* a size is < 1, or sizes overflow the index range    */
+  FA_ERR_UNSUPPORTED = -3,  /* valid but not implemented: head dim, dtype, size    */
+  FA_ERR_WORKSPACE = -4,    /* decode workspace NULL or smaller than required      */
+  FA_ERR_HIP = -5,          /* the HIP runtime reported an error at launch         */
+  FA_ERR_VALUE = -6,        /* scale not finite and > 0, causal not 0/1, ...       */
+  FA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned             */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
+
+/*
+ * fa_fwd — attention forward (prefill): every query row of every (b, h).
+ *   q   [B][H][Nq][d]  dtype          k, v [B][H][Nk][d]  dtype
+ *   o   [B][H][Nq][d]  float32 (written)
+ *   lse [B][H][Nq]     float32 (written) or NULL to skip it
+ *   d in {64, 128}; B, H, Nq, Nk >= 1 (ragged sizes allowed); Nk * d <= 2^30.
+ *   scale: finite and > 0 (1/sqrt(d) for standard attention).
+ *   causal: 0 or 1.
+ * bf16 inputs use bf16 MFMA with float32 accumulation; float32 inputs use
+ * float32 MFMA and never round to a narrower type.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * fa_decode_workspace_bytes — bytes of device workspace fa_decode_splitkv needs:
+ * B*H*num_splits*(d+2)*4. Returns 0 if an argument is < 1 or the size overflows.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * fa_decode_splitkv — one query per (b, h) against a long key/value cache
+ * (Flash-Decoding). The Nk keys are cut into num_splits chunks of
+ * C = ceil(Nk / num_splits) keys (trailing chunks may be short or empty); one
+ * pass computes each chunk's partial state (m, l, o) relative to the chunk's own
+ * max, and a second pass merges the partials in fixed order (deterministic).
+ *   q [B][H][1][d]  dtype        k, v [B][H][Nk][d]  dtype
+ *   o [B][H][1][d]  float32      lse [B][H][1] float32 or NULL
+ *   workspace: device memory of at least fa_decode_workspace_bytes(B, H, d,
+ *   num_splits) bytes, 16-byte aligned, owned by the caller; its contents on
+ *   entry are ignored and on return are unspecified. Not causal (a single query
+ *   at the end of the sequence sees every key).
+ *   d = 128 (FA_BF16 or FA_F32) or d = 64; 1 <= num_splits <= 1024; Nk >= 1.
+ */
+fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                            int B, int H, int Nk, int d, float scale, int num_splits,
+                            void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                            void* stream);
+
+/* fa_status_str — static English description of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/*
+ * fa_last_hip_error — the hipError_t (as int) behind the most recent FA_ERR_HIP returned
+ * on the calling thread; 0 (hipSuccess) if there was none. fa_last_hip_error_str gives
+ * the HIP runtime's name for it (never NULL).
+ */
+int fa_last_hip_error(void);
+const char* fa_last_hip_error_str(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -59,10 +59,12 @@ def _load():
 
 
 def default_threads() -> int:
+    """Host cores this process may use, capped at 16 (the CPU share of one GPU)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _as_input(x):

@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_08_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# a fake, 16-byte aligned, never dereferenced "device" address: validation must reject the
+# call before anything touches it
+P = 0x10000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared_functions() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    # and from the dynamic symbol table directly, as a C caller would see it
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for name in _declared_functions():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for st in range(-7, 1):
+        s = fa.status_str(st)
+        assert s and s != "unknown status"
+    assert fa.status_str(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert fa.decode_workspace_bytes(16, 32, 128, 64) == 16 * 32 * 64 * 130 * 4 == 17039360
+    assert fa.decode_workspace_bytes(1, 1, 64, 1) == 66 * 4
+    for bad in [(0, 1, 64, 1), (1, 0, 64, 1), (1, 1, 0, 1), (1, 1, 64, 0), (-1, 1, 64, 1)]:
+        assert fa.decode_workspace_bytes(*bad) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0,
+             dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                               a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(k=None), fa.FA_ERR_NULL),
+    (dict(v=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=0), fa.FA_ERR_SHAPE), (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(Nk=0), fa.FA_ERR_SHAPE), (dict(d=0), fa.FA_ERR_SHAPE), (dict(Nq=-5), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED), (dict(Nk=1 << 25, d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(scale=-1.0), fa.FA_ERR_VALUE),
+    (dict(scale=float("inf")), fa.FA_ERR_VALUE), (dict(scale=float("nan")), fa.FA_ERR_VALUE),
+    (dict(causal=2), fa.FA_ERR_VALUE),
+    (dict(q=P + 8), fa.FA_ERR_ALIGN), (dict(k=P + 2), fa.FA_ERR_ALIGN),
+    (dict(v=P + 4), fa.FA_ERR_ALIGN), (dict(o=P + 12), fa.FA_ERR_ALIGN),
+])
+def test_fwd_rejects(kw, status):
+    assert _fwd(**kw) == status
+
+
+def _dec(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=2, Nk=100, d=128, scale=0.1, S=4, ws=P,
+             wsb=fa.decode_workspace_bytes(2, 2, 128, 4), dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_decode_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                          a["Nk"], a["d"], a["scale"], a["S"], a["ws"], a["wsb"],
+                                          a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(Nk=0), fa.FA_ERR_SHAPE), (dict(S=0), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED), (dict(S=1025, wsb=1 << 30), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(scale=float("nan")), fa.FA_ERR_VALUE),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=fa.decode_workspace_bytes(2, 2, 128, 4) - 1), fa.FA_ERR_WORKSPACE),
+    (dict(ws=P + 4), fa.FA_ERR_ALIGN), (dict(q=P + 2), fa.FA_ERR_ALIGN),
+])
+def test_decode_rejects(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_python_layer_maps_errors_without_gpu():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)              # CPU tensors are refused before the library is called
+    with pytest.raises(ValueError):
+        fa._raise(fa.FA_ERR_SHAPE, "t")
+    with pytest.raises(NotImplementedError):
+        fa._raise(fa.FA_ERR_UNSUPPORTED, "t")
+    with pytest.raises(fa.FaError):
+        fa._raise(fa.FA_ERR_HIP, "t")
+
+
+def test_single_hip_runtime_in_process():
+    """libfa.so must bind to the HIP runtime torch already loaded, not load a second copy
+    (a second runtime has its own device context and reports no device)."""
+    fa.library()
+    maps = open("/proc/self/maps").read()
+    runtimes = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(runtimes) == 1, runtimes
