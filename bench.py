@@ -1,0 +1,228 @@
+"""Benchmark of the attention forward on one MI355X, with roofline and CPU-oracle context.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-extra] [--no-cpu]
+
+One step is one fa_fwd call (the whole prefill path: work mapping, K/V streaming,
+QK^T and PV on MFMA, online softmax, epilogue) over the workload's full batch, with the
+inputs resident in HBM. The headline workload is the causal N=8192, d=128 prefill that
+the throughput target is stated on; the N=30000 causal prefill and the split-KV decode
+are timed after it and reported in the same JSON line under "also".
+
+Prints ONE JSON line. `roofline.achieved` is the algorithmic FLOPs (4*B*H*Nq*Nk*d,
+halved for causal) of one launch divided by the kernel's average duration from HIP
+events on the launch stream; `cpu_baseline` times the float64 oracle on a bounded row
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA and vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak (prefill); HBM GB/s (decode)"
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "fwd_bf16": ["exact_tiled_attention_08_amd/csrc/fa_fwd_bf16.hip",
+                 "exact_tiled_attention_08_amd/csrc/fa_internal.h"],
+    "decode": ["exact_tiled_attention_08_amd/csrc/fa_decode.hip",
+               "exact_tiled_attention_08_amd/csrc/fa_internal.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kind: str, workload: int):
+    """HBM bytes per launch measured by rocprofv3 counters, or None if not measured for the
+    current kernel source (the record carries the source hash it was taken with)."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(f"{kind}:{workload}")
+    if not ent or ent.get("source_hash") != source_hash(kind):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """(wall ms per step, event ms per launch). fn launches on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, start.elapsed_time(stop) / steps
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """Time the oracle on a row sample sized for about target_s seconds; report the
+    algorithmic rate (same FLOP convention as the GPU figure)."""
+    import numpy as np
+    import oracle
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    threads = oracle.default_threads()
+    total_rows = w.B * w.H * w.Nq
+
+    def row_flops(rows):
+        i = np.asarray(rows) % w.Nq
+        keys = np.minimum(w.Nk, i + (w.Nk - w.Nq) + 1) if w.causal else np.full(i.shape, w.Nk)
+        return float(4.0 * w.d * keys.sum())
+
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(total_rows, size=min(total_rows, 256), replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(qc, kc, vc, w.scale, w.causal, rows=probe, threads=threads)
+    rate = row_flops(probe) / max(1e-6, time.perf_counter() - t0)
+    per_row = row_flops(probe) / len(probe)
+    n = int(min(total_rows, max(256, target_s * rate / per_row)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(qc, kc, vc, w.scale, w.causal, rows=rows, threads=threads)
+    sec = time.perf_counter() - t0
+    flops = row_flops(rows)
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows (uniform random, seed 0) of the same "
+                      f"workload, all their visible keys; {flops / 1e9:.1f} GFLOP in {sec:.1f} s"}
+
+
+def prefill_record(num: int, steps: int, warmup: int):
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[num]
+    q, k, v = W.make_inputs(w, "cuda")
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    achieved = w.flops / (ev_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+    rec = {
+        "workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+        "causal": w.causal, "flops_per_launch": w.flops,
+        "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic_for("fwd_bf16", num)},
+    }
+    return rec, (w, q, k, v)
+
+
+def decode_record(steps: int, warmup: int):
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[5]
+    q, k, v = W.make_inputs(w, "cuda")
+    ws = torch.empty((fa.decode_workspace_bytes(w.B, w.H, w.d, w.num_splits),), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((w.B, w.H, 1, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.decode(q, k, v, num_splits=w.num_splits, scale=w.scale, out=o, lse=lse, workspace=ws)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    achieved = w.io_bytes / (ev_ms * 1e-3) / 1e9
+    rec = {
+        "workload": w.name, "B": w.B, "H": w.H, "Nk": w.Nk, "d": w.d, "num_splits": w.num_splits,
+        "bytes_per_call": w.io_bytes, "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "note": "kernel_ms spans both launches of one call (split + merge)",
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for("decode", 5)},
+    }
+    del q, k, v
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one leg only (used under the profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path shards over (batch, head) with no exchange, "
+              "and runs on more than one GPU are not part of this build; use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.only == "decode":
+        rec = decode_record(args.steps, args.warmup)
+        print(json.dumps({"decode": rec}), flush=True)
+        return
+
+    main_rec, (w, q, k, v) = prefill_record(args.workload, args.steps, args.warmup)
+    out = {
+        "metric": METRIC,
+        "value": main_rec["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs; no dataset)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "global_batch": w.B, "seq_len": w.Nq, "parallelism": "none"},
+        "roofline": main_rec["roofline"],
+        "kernel_ms": main_rec["kernel_ms"],
+    }
+    if args.only is None and not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    del q, k, v
+    torch.cuda.empty_cache()
+    if args.only is None and not args.no_extra:
+        extra = {}
+        rec4, _ = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
+        extra["prefill_N30000"] = rec4
+        torch.cuda.empty_cache()
+        extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
+        out["also"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
