@@ -19,6 +19,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed float32 VALU ops (v_pk_fma_f32 and kin)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # inputs with NaN are outside the contract: lets fmaxf lower to plain v_max/v_max3
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]

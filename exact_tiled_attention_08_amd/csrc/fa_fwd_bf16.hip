@@ -1,60 +1,85 @@
 // Attention forward for bfloat16 Q/K/V on gfx950: bf16 MFMA, float32 accumulation.
 //
-// One workgroup owns BR = 32*NW query rows of one (b, h); each of its NW waves owns
-// 32 rows. K and V stream through LDS in tiles of BC keys (double-buffered), and each
-// wave folds every tile into its running state with the online-softmax recurrence:
+// One workgroup owns BR = 32*NW query rows of one (b, h); each of its NW waves owns 32
+// rows. K and V stream through LDS in tiles of BC keys (two stages), and each wave folds
+// every tile into its running state with the online-softmax recurrence:
 // "FlashAttention: Attention Is Limited by Memory, Not Math", section "How tiling and
 // online softmax stay exact" (running max m and sum l; previous sums rescaled by
 // exp(m_old - m_new) when the max rises; divide by l once at the end), and
 // "Explain FlashAttention ...", section "Keep only the state needed for the final
-// weighted average". The loop order is the one that reads each query block once and
-// streams all key/value blocks past it ("Flash Attention Optimization", section
-// "Active recall", question 6 and its answer), with the query tiles of all heads as
-// independent workgroups ("FlashAttention 1, 2 and 3": parallel over sequence length
-// as well as batch and heads).
+// weighted average". Each query block is read once and every key/value block streams
+// past it ("Flash Attention Optimization", section "Active recall", question 6 and its
+// answer); the query tiles of all heads are independent workgroups ("FlashAttention 1, 2
+// and 3": parallel over sequence length as well as batch and heads).
 //
 // Register layouts (v_mfma_f32_32x32x16_bf16, lane l, g = l / 32):
 //   A operand (32 x 16): row l%32, k = 8g..8g+7      B operand (16 x 32): col l%32, same k
 //   C (32 x 32):        col l%32, row 8*(i/4) + 4g + i%4 for element i = 0..15
-// The kernel computes S^T = K Q^T, so each lane's accumulator column is ONE query row
-// and its 16 elements are 16 keys: the row max and row sum are in-lane except for one
-// exchange with lane l^32, and the S^T accumulator converts in place into the P^T
-// operand of O^T = V^T P^T. The key order inside the PV contraction is permuted to
-// match; V is written to LDS transposed in that same permuted key order.
+// The kernel computes S^T = K Q^T, so each lane's accumulator column is ONE query row and
+// its 16 elements are 16 keys: the row max and row sum are in-lane except for one swap
+// between the two lane halves (v_permlane32_swap), and the S^T accumulator converts in
+// place into the P^T operand of O^T = V^T P^T. Inside each 16-key step of the PV
+// contraction lane half g carries keys {4g..4g+3, 8+4g..8+4g+3}; the V^T operand is read
+// in exactly that key order with the LDS transpose read ds_read_b64_tr_b16, so V stays
+// row-major in LDS.
+//
+// Memory path: K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at LDS base + 16*i), so no
+// VGPRs stage them. Rows are stored unpadded with an XOR swizzle of their 16-byte chunks
+// so that the fragment reads are free of bank conflicts. Key rows past Nk are clamped to
+// row Nk-1 (finite data that the mask then zero-weights).
+//
+// Rescaling: the accumulator is rescaled only in tiles where some row of the wave raised
+// its running max; in the other tiles alpha = 1 for every row and the multiply is skipped.
+// The offset is always the exact running max, so the largest weight of a row is exactly
+// 1 and survives the rounding of P to bfloat16 without error (an offset that lags the
+// max would leave the dominant weight at 2^delta, rounded by up to 2^-9 of its size).
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void gbl_void;
+
 template <int D, int BC, int NW>
 struct Cfg {
   static constexpr int BR = 32 * NW;          // query rows per workgroup
   static constexpr int T = 64 * NW;           // threads per workgroup
-  static constexpr int KPITCH = D * 2 + 16;   // bytes per K row in LDS (16 B pad: no bank conflicts)
-  static constexpr int VPITCH = BC * 2 + 16;  // bytes per V^T row in LDS
-  static constexpr int KBYTES = BC * KPITCH;
-  static constexpr int VBYTES = D * VPITCH;
-  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int ROWB = D * 2;          // bytes per K or V row in LDS (unpadded)
+  static constexpr int CHR = D / 8;           // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;     // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILEB;     // K tile then V tile
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int KCHUNKS = BC * D / 8;        // 16-byte pieces of a K tile
-  static constexpr int VUNITS = (BC / 4) * (D / 8); // 4-key x 8-dim pieces of a V tile
-  static constexpr int KPER = (KCHUNKS + T - 1) / T;
-  static constexpr int VPER = (VUNITS + T - 1) / T;
-  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+  static constexpr int SLOTS = BC * CHR;      // 16-byte slots per tile
+  static constexpr int LOADS = SLOTS / T;     // direct loads per thread per tensor per tile
+  static constexpr int ROWSTEP = T / CHR;     // rows between a thread's successive slots
+  static_assert(D % 32 == 0 && BC % 32 == 0 && CHR >= 8, "tile shape");
+  static_assert(SLOTS % T == 0 && T % CHR == 0, "slots must split evenly over threads");
   static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
 };
 
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) {  // {a.lo, b.lo}
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+// XOR swizzles of the 16-byte chunk position within a row (bijective per row).
+template <int CHR>
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & (CHR - 1)); }
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 1); }
+
+__device__ __forceinline__ float wave_half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {  // {a.hi, b.hi}
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+__device__ __forceinline__ float wave_half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, int BC, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D, BC, NW>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,156 +117,128 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
   }
   const int ntiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
-  uint4 kreg[C::KPER];
-  uint4 vreg[C::VPER][4];
-
-  auto load_tile = [&](int t) {
+  // Direct-load slots of this thread: slot s = n*T + tid -> row s / CHR, chunk position
+  // s % CHR; the chunk fetched is the one the swizzle stores at that position.
+  const int lrow = tid / C::CHR;
+  const int lpos = tid % C::CHR;
+  auto issue_tile = [&](int t, int stage) {
     const int kv0 = t * BC;
-#pragma unroll
-    for (int n = 0; n < C::KPER; ++n) {
-      const int ch = tid + n * C::T;
-      const int row = ch / (D / 8), cc = ch % (D / 8);
-      const int key = kv0 + row;
-      kreg[n] = (ch < C::KCHUNKS && key < p.Nk)
-                    ? *(const uint4*)(kh + (size_t)key * D + 8 * cc)
-                    : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int n = 0; n < C::VPER; ++n) {
-      const int u = tid + n * C::T;
-      const int dc = u % (D / 8), kq = u / (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + 4 * kq + r;
-        vreg[n][r] = (u < C::VUNITS && key < p.Nk)
-                         ? *(const uint4*)(vh + (size_t)key * D + 8 * dc)
-                         : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
     char* Ks = smem + stage * C::STAGE;
-    char* Vs = Ks + C::KBYTES;
+    char* Vs = Ks + C::TILEB;
 #pragma unroll
-    for (int n = 0; n < C::KPER; ++n) {
-      const int ch = tid + n * C::T;
-      if (ch < C::KCHUNKS) {
-        const int row = ch / (D / 8), cc = ch % (D / 8);
-        *(uint4*)(Ks + row * C::KPITCH + cc * 16) = kreg[n];
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < C::VPER; ++n) {
-      const int u = tid + n * C::T;
-      if (u < C::VUNITS) {
-        const int dc = u % (D / 8), kq = u / (D / 8);
-        // keys 4kq..4kq+3 = 16c + 8a + 4g' + r land at V^T columns 16c + 8g' + 4a + r
-        const int pos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
-        const uint4 x0 = vreg[n][0], x1 = vreg[n][1], x2 = vreg[n][2], x3 = vreg[n][3];
-        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
-        const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
-        const uint32_t a2[4] = {x2.x, x2.y, x2.z, x2.w};
-        const uint32_t a3[4] = {x3.x, x3.y, x3.z, x3.w};
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          uint2 ev, od;
-          ev.x = lo16x2(a0[wd], a1[wd]);
-          ev.y = lo16x2(a2[wd], a3[wd]);
-          od.x = hi16x2(a0[wd], a1[wd]);
-          od.y = hi16x2(a2[wd], a3[wd]);
-          *(uint2*)(Vs + (8 * dc + 2 * wd) * C::VPITCH + pos * 2) = ev;
-          *(uint2*)(Vs + (8 * dc + 2 * wd + 1) * C::VPITCH + pos * 2) = od;
-        }
-      }
+    for (int n = 0; n < C::LOADS; ++n) {
+      const int r = lrow + n * C::ROWSTEP;
+      const int key = min(kv0 + r, p.Nk - 1);
+      const int ck = swz_k<C::CHR>(r, lpos);
+      const int cv = swz_v(r, lpos);
+      const int wave_slot = (n * C::T + 64 * w) * 16;  // wave-uniform LDS byte offset
+      // uniform 64-bit head base + 32-bit byte offset (the saddr + voffset load form)
+      const uint32_t koff = (uint32_t)(key * (2 * D) + 16 * ck);
+      const uint32_t voff = (uint32_t)(key * (2 * D) + 16 * cv);
+      __builtin_amdgcn_global_load_lds((const gbl_void*)((const char*)kh + koff),
+                                       (lds_void*)(Ks + wave_slot), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const gbl_void*)((const char*)vh + voff),
+                                       (lds_void*)(Vs + wave_slot), 16, 0, 0);
     }
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY;  // running max of this lane's row, in units of log2 (score * c)
+  float m = -INFINITY;  // running offset of this lane's row, in log2 units (score * c)
   float l = 0.f;        // running sum over this lane's half of the keys
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // per-lane constants of the V^T transpose reads
+  const int trG = (lane >> 4) & 1;  // which 16 of the 32 output dims
+  const int trj = lane & 15;
+
+  if (ntiles > 0) issue_tile(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // my slots of tile t have landed
+    __syncthreads();  // everyone's have; everyone is done with tile t-1's stage
+    if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
     const int kv0 = t * BC;
-    if (kv0 < wave_kv_end) {
-      const char* Ks = smem + (t & 1) * C::STAGE;
-      const char* Vs = Ks + C::KBYTES;
+    if (kv0 >= wave_kv_end) continue;  // whole tile above the diagonal for this wave
+    const char* Ks = smem + (t & 1) * C::STAGE;
+    const char* Vs = Ks + C::TILEB;
 
-      // S^T tile = K_j Q_i^T  (BC keys x 32 queries per wave)
-      f32x16 s[BC / 32];
+    // S^T tile = K_j Q_i^T  (BC keys x 32 queries per wave)
+    f32x16 s[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        s[kb] = f32x16{};
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      s[kb] = f32x16{};
+      const int r = 32 * kb + col;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 ka = *(const bf16x8*)(Ks + (32 * kb + col) * C::KPITCH + (16 * kk + 8 * g) * 2);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], s[kb], 0, 0, 0);
-        }
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 ka = *(const bf16x8*)(Ks + r * C::ROWB + swz_k<C::CHR>(r, 2 * kk + g) * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], s[kb], 0, 0, 0);
       }
+    }
 
-      // Mask on absolute positions: only tiles that cross the key tail or the diagonal.
-      const bool need_mask = (kv0 + BC > p.Nk) || (CAUSAL && kv0 + BC - 1 > wq0 + p.off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > lim) s[kb][i] = -INFINITY;
-          }
-      }
-
-      // Online softmax: new running max, rescale factor, exponentials.
-      float mx = -INFINITY;
+    // Mask on absolute positions: only tiles that cross the key tail or the diagonal.
+    const bool need_mask = (kv0 + BC > p.Nk) || (CAUSAL && kv0 + BC - 1 > wq0 + p.off);
+    if (need_mask) {
+      // key kv0 + 32kb + 8(i/4) + 4g + i%4 is visible iff its in-tile offset <= lim
+      const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - kv0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx * p.c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // empty so far: any offset
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      m = m_new;
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
+    }
 
-      bf16x8 pb[BC / 16];
-      float lsum = 0.f;
+    // Online softmax; the rescale of O is skipped when no row of the wave raised its max.
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], p.c, -m_use));
-          lsum += e;
-          pb[2 * kb + (i >> 3)][i & 7] = (__bf16)e;  // round to nearest even
-        }
-      l = l * alpha + lsum;
-
-      // O^T = alpha * O^T + V_j^T P^T
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    const float mt = wave_half_max(mx) * p.c;  // tile row max, log2 units (-inf if masked)
+    const bool raise = mt > m;
+    if (__any(raise)) {
+      // rows that raised: alpha = exp(m_old - m_new) (0 when m_old = -inf); others: 1
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+      m = raise ? mt : m;
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 va = *(const bf16x8*)(Vs + (32 * db + col) * C::VPITCH + (16 * kc + 8 * g) * 2);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], oacc[db], 0, 0, 0);
-        }
     }
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
-    __syncthreads();
+    const float m_use = (m == -INFINITY) ? 0.f : m;  // nothing visible yet: weights are 0
+
+    bf16x8 pb[BC / 16];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], p.c, -m_use));
+        lsum += e;
+        pb[2 * kb + (i >> 3)][i & 7] = (__bf16)e;  // round to nearest even
+      }
+    l += lsum;
+
+    // O^T += V_j^T P^T; the V^T operand comes from two transpose reads per 16-key step.
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        bf16x4 half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 16 * kc + 8 * h + 4 * g + (trj >> 2);
+          const int cbyte = 64 * db + 32 * trG + 8 * (trj & 3);
+          const int addr = r * C::ROWB + swz_v(r, cbyte >> 4) * 16 + (cbyte & 15);
+          half[h] = __builtin_bit_cast(
+              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + addr)));
+        }
+        const bf16x8 va = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], oacc[db], 0, 0, 0);
+      }
   }
 
   // Epilogue: divide by l once; LSE = ln2 * (m + log2 l). Empty row: O = 0, LSE = -inf.
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = wave_half_sum(l);
   if (qrow < p.Nq) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float* orow = p.o + ((size_t)bh * p.Nq + qrow) * D;
@@ -274,7 +271,7 @@ hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
 
 }  // namespace
 
-int fwd_bf16_block_rows(int d) { return d == 64 ? 32 * 4 : 32 * 4; }
+int fwd_bf16_block_rows(int) { return 32 * 4; }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s) {
   if (d == 128) return launch<128, 64, 4>(p, causal, s);
