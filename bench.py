@@ -164,6 +164,17 @@ def decode_record(steps: int, warmup: int):
     return rec
 
 
+def copy_record(steps: int, warmup: int):
+    """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30 bytes each."""
+    import torch
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    wall_ms, ev_ms = time_launches(lambda: y.copy_(x), steps, warmup)
+    return {"bytes_read": 2 * n, "bytes_written": 2 * n, "kernel_ms": ev_ms,
+            "GBps": 4 * n / (ev_ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,8 +184,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run one leg only (used under the profiler)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one leg only (used under the profiler); 'copy' times a plain "
+                         "1 GiB device copy, the reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path shards over (batch, head) with no exchange, "
@@ -190,8 +202,14 @@ def main():
         rec = decode_record(args.steps, args.warmup)
         print(json.dumps({"decode": rec}), flush=True)
         return
+    if args.only == "copy":
+        print(json.dumps({"copy": copy_record(args.steps, args.warmup)}), flush=True)
+        return
 
     main_rec, (w, q, k, v) = prefill_record(args.workload, args.steps, args.warmup)
+    if args.only == "prefill":
+        print(json.dumps({"prefill": main_rec}), flush=True)
+        return
     out = {
         "metric": METRIC,
         "value": main_rec["tflops"],

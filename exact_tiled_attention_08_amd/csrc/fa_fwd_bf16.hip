@@ -62,10 +62,22 @@ struct Cfg {
   static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
 };
 
-// XOR swizzles of the 16-byte chunk position within a row (bijective per row).
+// XOR swizzles of the 16-byte chunk position within a row (bijective per row). LDS has 64
+// banks of 4 bytes; a 16-byte read is served 16 lanes at a time and an 8-byte read 32
+// lanes at a time, so each such group must touch distinct banks:
+//  - K reads (ds_read_b128): 16 lanes read 16 consecutive rows at one chunk.
+//  - V transpose reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows at 4
+//    consecutive chunks (both 8-byte halves of each).
+// With 256-byte rows (d = 128) a row spans all banks, so rows must differ in chunk
+// position; with 128-byte rows (d = 64) odd rows already sit in the upper 32 banks.
 template <int CHR>
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & (CHR - 1)); }
-__device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 1); }
+__device__ __forceinline__ int swz_k(int r, int c) {
+  return CHR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+template <int CHR>
+__device__ __forceinline__ int swz_v(int r, int c) {
+  return CHR == 16 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
+}
 
 __device__ __forceinline__ float wave_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -83,7 +95,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
   const int g = lane >> 5;
   const int col = lane & 31;
 
@@ -121,24 +133,35 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
   // s % CHR; the chunk fetched is the one the swizzle stores at that position.
   const int lrow = tid / C::CHR;
   const int lpos = tid % C::CHR;
+  uint32_t koff[C::LOADS], voff[C::LOADS];  // byte offsets within a tile of keys
+#pragma unroll
+  for (int n = 0; n < C::LOADS; ++n) {
+    const int r = lrow + n * C::ROWSTEP;
+    koff[n] = (uint32_t)(r * C::ROWB + 16 * swz_k<C::CHR>(r, lpos));
+    voff[n] = (uint32_t)(r * C::ROWB + 16 * swz_v<C::CHR>(r, lpos));
+  }
   auto issue_tile = [&](int t, int stage) {
     const int kv0 = t * BC;
     char* Ks = smem + stage * C::STAGE;
     char* Vs = Ks + C::TILEB;
+    // uniform 64-bit tile base + 32-bit per-lane offset (the saddr + voffset load form)
+    const char* kt = (const char*)kh + (size_t)kv0 * C::ROWB;
+    const char* vt = (const char*)vh + (size_t)kv0 * C::ROWB;
+    const bool tail = kv0 + BC > p.Nk;  // rows past Nk re-read row Nk-1 instead
 #pragma unroll
     for (int n = 0; n < C::LOADS; ++n) {
-      const int r = lrow + n * C::ROWSTEP;
-      const int key = min(kv0 + r, p.Nk - 1);
-      const int ck = swz_k<C::CHR>(r, lpos);
-      const int cv = swz_v(r, lpos);
+      uint32_t ko = koff[n], vo = voff[n];
+      if (tail) {
+        const int r = lrow + n * C::ROWSTEP;
+        const int back = max(0, kv0 + r - (p.Nk - 1)) * C::ROWB;
+        ko -= back;
+        vo -= back;
+      }
       const int wave_slot = (n * C::T + 64 * w) * 16;  // wave-uniform LDS byte offset
-      // uniform 64-bit head base + 32-bit byte offset (the saddr + voffset load form)
-      const uint32_t koff = (uint32_t)(key * (2 * D) + 16 * ck);
-      const uint32_t voff = (uint32_t)(key * (2 * D) + 16 * cv);
-      __builtin_amdgcn_global_load_lds((const gbl_void*)((const char*)kh + koff),
-                                       (lds_void*)(Ks + wave_slot), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const gbl_void*)((const char*)vh + voff),
-                                       (lds_void*)(Vs + wave_slot), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const gbl_void*)(kt + ko), (lds_void*)(Ks + wave_slot),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const gbl_void*)(vt + vo), (lds_void*)(Vs + wave_slot),
+                                       16, 0, 0);
     }
   };
 
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
         for (int h = 0; h < 2; ++h) {
           const int r = 16 * kc + 8 * h + 4 * g + (trj >> 2);
           const int cbyte = 64 * db + 32 * trG + 8 * (trj & 3);
-          const int addr = r * C::ROWB + swz_v(r, cbyte >> 4) * 16 + (cbyte & 15);
+          const int addr = r * C::ROWB + swz_v<C::CHR>(r, cbyte >> 4) * 16 + (cbyte & 15);
           half[h] = __builtin_bit_cast(
               bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + addr)));
         }
