@@ -16,7 +16,7 @@ SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     # keep the compiler from emitting packed float32 VALU ops (v_pk_fma_f32 and kin)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # inputs with NaN are outside the contract: lets fmaxf lower to plain v_max/v_max3

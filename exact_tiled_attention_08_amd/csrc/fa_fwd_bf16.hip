@@ -1,16 +1,15 @@
 // Attention forward for bfloat16 Q/K/V on gfx950: bf16 MFMA, float32 accumulation.
 //
-// One workgroup owns BR = 32*NW query rows of one (b, h); each of its NW waves owns 32
-// rows. K and V stream through LDS in tiles of BC keys (two stages), and each wave folds
-// every tile into its running state with the online-softmax recurrence:
-// "FlashAttention: Attention Is Limited by Memory, Not Math", section "How tiling and
-// online softmax stay exact" (running max m and sum l; previous sums rescaled by
-// exp(m_old - m_new) when the max rises; divide by l once at the end), and
-// "Explain FlashAttention ...", section "Keep only the state needed for the final
-// weighted average". Each query block is read once and every key/value block streams
-// past it ("Flash Attention Optimization", section "Active recall", question 6 and its
-// answer); the query tiles of all heads are independent workgroups ("FlashAttention 1, 2
-// and 3": parallel over sequence length as well as batch and heads).
+// One workgroup owns BR = 256 query rows of one (b, h); each of its 8 waves owns 32 rows.
+// K and V stream through LDS in tiles of BC keys, and each wave folds every tile into its
+// running state with the online-softmax recurrence: "FlashAttention: Attention Is Limited
+// by Memory, Not Math", section "How tiling and online softmax stay exact" (running max m
+// and sum l; previous sums rescaled by exp(m_old - m_new) when the max rises; divide by l
+// once at the end), and "Explain FlashAttention ...", section "Keep only the state needed
+// for the final weighted average". Each query block is read once and every key/value block
+// streams past it ("Flash Attention Optimization", section "Active recall", question 6
+// and its answer); the query tiles of all heads are independent workgroups
+// ("FlashAttention 1, 2 and 3": parallel over sequence length as well as batch and heads).
 //
 // Register layouts (v_mfma_f32_32x32x16_bf16, lane l, g = l / 32):
 //   A operand (32 x 16): row l%32, k = 8g..8g+7      B operand (16 x 32): col l%32, same k
@@ -29,11 +28,17 @@
 // so that the fragment reads are free of bank conflicts. Key rows past Nk are clamped to
 // row Nk-1 (finite data that the mask then zero-weights).
 //
-// Rescaling: the accumulator is rescaled only in tiles where some row of the wave raised
-// its running max; in the other tiles alpha = 1 for every row and the multiply is skipped.
-// The offset is always the exact running max, so the largest weight of a row is exactly
-// 1 and survives the rounding of P to bfloat16 without error (an offset that lags the
-// max would leave the dominant weight at 2^delta, rounded by up to 2^-9 of its size).
+// Schedule: the 8 waves form two groups of 4 (one wave of each group per SIMD). A group
+// alternates a matrix phase (S for the next tile and PV for the current tile, all MFMA)
+// with a vector phase (mask, online softmax, rescale of O), and the groups run half a
+// step apart, separated by workgroup barriers: while one group's waves keep a SIMD's
+// matrix core busy, the other group's waves use its vector ALU. Group 0 also issues the
+// direct loads of the next K and V tiles, two phases ahead of their first use.
+//
+// Rescaling: the offset is always the exact running max, so the largest weight of a row
+// is exactly 1 and survives the rounding of P to bfloat16 without error (an offset that
+// lags the max would leave the dominant weight at 2^delta, rounded by up to 2^-9 of its
+// size); the multiply of O is skipped when no row of the wave raised its max.
 #include "fa_internal.h"
 
 namespace fa {
@@ -42,23 +47,25 @@ namespace {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void gbl_void;
+typedef __attribute__((address_space(3))) char lds_char;
 
-template <int D, int BC, int NW>
+constexpr int kNW = 8;  // waves per workgroup: two groups of four
+
+template <int D, int BC>
 struct Cfg {
-  static constexpr int BR = 32 * NW;          // query rows per workgroup
-  static constexpr int T = 64 * NW;           // threads per workgroup
+  static constexpr int BR = 32 * kNW;         // query rows per workgroup
+  static constexpr int T = 64 * kNW;          // threads per workgroup
+  static constexpr int TL = T / 2;            // threads that issue loads (group 0)
   static constexpr int ROWB = D * 2;          // bytes per K or V row in LDS (unpadded)
   static constexpr int CHR = D / 8;           // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;     // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TILEB;     // K tile then V tile
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = 4 * TILEB;       // two K buffers, two V buffers
   static constexpr int SLOTS = BC * CHR;      // 16-byte slots per tile
-  static constexpr int LOADS = SLOTS / T;     // direct loads per thread per tensor per tile
-  static constexpr int ROWSTEP = T / CHR;     // rows between a thread's successive slots
+  static constexpr int LOADS = SLOTS / TL;    // direct loads per loading thread per tile
+  static constexpr int ROWSTEP = TL / CHR;    // rows between a thread's successive slots
   static_assert(D % 32 == 0 && BC % 32 == 0 && CHR >= 8, "tile shape");
-  static_assert(SLOTS % T == 0 && T % CHR == 0, "slots must split evenly over threads");
+  static_assert(SLOTS % TL == 0 && TL % CHR == 0, "slots must split evenly over threads");
+  static_assert(ROWSTEP % 16 == 0, "swizzles must repeat every ROWSTEP rows");
   static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
 };
 
@@ -79,6 +86,34 @@ __device__ __forceinline__ int swz_v(int r, int c) {
   return CHR == 16 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
 }
 
+// Workgroup barrier without the memory fence of __syncthreads(): the fence would also wait
+// for this wave's in-flight direct-to-LDS loads, which must keep flying across the phase
+// barrier. LDS reads are drained first; loads are waited for explicitly where their data
+// is needed. The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One global_load_lds_dwordx4: each lane copies 16 bytes from (uniform base + its 32-bit
+// byte offset) to LDS byte address lds_base + 16*lane (lds_base wave-uniform, in M0).
+// Written as inline asm so that the compiler does not treat later LDS reads of OTHER
+// buffers as possible readers of this copy and stall them on vmcnt; completion is awaited
+// explicitly with wait_loads() before the barrier that publishes the buffer. The offset
+// register is the caller's long-lived VGPR, so no later instruction overwrites it while
+// the load is in flight. M0 is saved and restored around the copy.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
 __device__ __forceinline__ float wave_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -88,14 +123,15 @@ __device__ __forceinline__ float wave_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
-  using C = Cfg<D, BC, NW>;
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
+  using C = Cfg<D, BC>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
+  const bool loader = w < kNW / 2;                          // group 0 issues the loads
   const int g = lane >> 5;
   const int col = lane & 31;
 
@@ -129,89 +165,88 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
   }
   const int ntiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
-  // Direct-load slots of this thread: slot s = n*T + tid -> row s / CHR, chunk position
-  // s % CHR; the chunk fetched is the one the swizzle stores at that position.
-  const int lrow = tid / C::CHR;
+  // Direct-load slots of a loading thread: slot s = n*TL + tid -> row s / CHR, chunk
+  // position s % CHR; the chunk fetched is the one the swizzle stores at that position.
+  // Both swizzles depend only on row bits that repeat every ROWSTEP rows, so one byte
+  // offset per tensor serves all of the thread's slots.
+  const int lrow = (tid % C::TL) / C::CHR;
   const int lpos = tid % C::CHR;
-  uint32_t koff[C::LOADS], voff[C::LOADS];  // byte offsets within a tile of keys
-#pragma unroll
-  for (int n = 0; n < C::LOADS; ++n) {
-    const int r = lrow + n * C::ROWSTEP;
-    koff[n] = (uint32_t)(r * C::ROWB + 16 * swz_k<C::CHR>(r, lpos));
-    voff[n] = (uint32_t)(r * C::ROWB + 16 * swz_v<C::CHR>(r, lpos));
-  }
-  auto issue_tile = [&](int t, int stage) {
+  const uint32_t koff = (uint32_t)(lrow * C::ROWB + 16 * swz_k<C::CHR>(lrow, lpos));
+  const uint32_t voff = (uint32_t)(lrow * C::ROWB + 16 * swz_v<C::CHR>(lrow, lpos));
+  auto kbuf = [&](int i) -> char* { return smem + i * C::TILEB; };
+  auto vbuf = [&](int i) -> char* { return smem + (2 + i) * C::TILEB; };
+  // Issue the direct loads of one tile of K (or V) into an LDS buffer (loading group only).
+  // Rows past Nk re-read row Nk-1.
+  auto issue = [&](const uint16_t* base, uint32_t off, int t, char* dst) {
     const int kv0 = t * BC;
-    char* Ks = smem + stage * C::STAGE;
-    char* Vs = Ks + C::TILEB;
-    // uniform 64-bit tile base + 32-bit per-lane offset (the saddr + voffset load form)
-    const char* kt = (const char*)kh + (size_t)kv0 * C::ROWB;
-    const char* vt = (const char*)vh + (size_t)kv0 * C::ROWB;
-    const bool tail = kv0 + BC > p.Nk;  // rows past Nk re-read row Nk-1 instead
+    const bool tail = kv0 + BC > p.Nk;
 #pragma unroll
     for (int n = 0; n < C::LOADS; ++n) {
-      uint32_t ko = koff[n], vo = voff[n];
-      if (tail) {
-        const int r = lrow + n * C::ROWSTEP;
-        const int back = max(0, kv0 + r - (p.Nk - 1)) * C::ROWB;
-        ko -= back;
-        vo -= back;
+      const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * w) * 16));
+      if (!tail) {
+        // uniform base of this slot row group + the thread's fixed in-group offset
+        dma16((const char*)base + (size_t)(kv0 + n * C::ROWSTEP) * C::ROWB, off, lds);
+      } else {
+        // tail tile: offset of the clamped row from the head base (< 2^31 bytes)
+        const int row = min(kv0 + lrow + n * C::ROWSTEP, p.Nk - 1);
+        dma16(base, (uint32_t)(row * C::ROWB) + (off - (uint32_t)(lrow * C::ROWB)), lds);
       }
-      const int wave_slot = (n * C::T + 64 * w) * 16;  // wave-uniform LDS byte offset
-      __builtin_amdgcn_global_load_lds((const gbl_void*)(kt + ko), (lds_void*)(Ks + wave_slot),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const gbl_void*)(vt + vo), (lds_void*)(Vs + wave_slot),
-                                       16, 0, 0);
     }
+  };
+
+  // S^T tile = K_j Q_i^T  (BC keys x 32 queries per wave). The BC/32 accumulators advance
+  // together along the contraction (consecutive MFMAs are independent), and the K
+  // fragments of step kk+2 are read from LDS while step kk's MFMAs run.
+  auto kfrag = [&](const char* Ks, int kb, int kk) {
+    const int r = 32 * kb + col;
+    return *(const bf16x8*)(Ks + r * C::ROWB + swz_k<C::CHR>(r, 2 * kk + g) * 16);
+  };
+  auto compute_s = [&](const char* Ks, f32x16 (&s)[BC / 32]) {
+    constexpr int NKB = BC / 32, NKK = D / 16, DIST = 2;
+    bf16x8 ka[DIST + 1][NKB];
+#pragma unroll
+    for (int kk = 0; kk < DIST; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) ka[kk][kb] = kfrag(Ks, kb, kk);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + DIST < NKK) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) ka[(kk + DIST) % (DIST + 1)][kb] = kfrag(Ks, kb, kk + DIST);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this step's MFMAs
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (DIST + 1)][kb], qb[kk], s[kb], 0, 0, 0);
+    }
+  };
+  // Mask on absolute positions, only for tiles that cross the key tail or the diagonal
+  // (a tile past the wave's keys is masked out entirely):
+  // key kv0 + 32kb + 8(i/4) + 4g + i%4 is visible iff its in-tile offset <= lim.
+  auto needs_mask = [&](int t) {
+    const int kv0 = t * BC;
+    return (kv0 + BC > p.Nk) || (CAUSAL && kv0 + BC - 1 > wq0 + p.off) || (kv0 >= wave_kv_end);
+  };
+  auto mask_s = [&](int t, f32x16 (&s)[BC / 32]) {
+    const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - t * BC - 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY;  // running offset of this lane's row, in log2 units (score * c)
+  float m = -INFINITY;  // running max of this lane's row, in log2 units (score * c)
   float l = 0.f;        // running sum over this lane's half of the keys
 
-  // per-lane constants of the V^T transpose reads
-  const int trG = (lane >> 4) & 1;  // which 16 of the 32 output dims
-  const int trj = lane & 15;
-
-  if (ntiles > 0) issue_tile(0, 0);
-
-  for (int t = 0; t < ntiles; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // my slots of tile t have landed
-    __syncthreads();  // everyone's have; everyone is done with tile t-1's stage
-    if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
-    const int kv0 = t * BC;
-    if (kv0 >= wave_kv_end) continue;  // whole tile above the diagonal for this wave
-    const char* Ks = smem + (t & 1) * C::STAGE;
-    const char* Vs = Ks + C::TILEB;
-
-    // S^T tile = K_j Q_i^T  (BC keys x 32 queries per wave)
-    f32x16 s[BC / 32];
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
-      s[kb] = f32x16{};
-      const int r = 32 * kb + col;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + r * C::ROWB + swz_k<C::CHR>(r, 2 * kk + g) * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], s[kb], 0, 0, 0);
-      }
-    }
-
-    // Mask on absolute positions: only tiles that cross the key tail or the diagonal.
-    const bool need_mask = (kv0 + BC > p.Nk) || (CAUSAL && kv0 + BC - 1 > wq0 + p.off);
-    if (need_mask) {
-      // key kv0 + 32kb + 8(i/4) + 4g + i%4 is visible iff its in-tile offset <= lim
-      const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - kv0 - 4 * g;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
-    }
-
-    // Online softmax; the rescale of O is skipped when no row of the wave raised its max.
+  // Online softmax of one tile; O is rescaled here, after the previous tile's PV and
+  // before this tile's, and only when some row of the wave raised its max.
+  auto softmax = [&](f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -219,17 +254,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     const float mt = wave_half_max(mx) * p.c;  // tile row max, log2 units (-inf if masked)
     const bool raise = mt > m;
-    if (__any(raise)) {
-      // rows that raised: alpha = exp(m_old - m_new) (0 when m_old = -inf); others: 1
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
-      m = raise ? mt : m;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-    }
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.f;  // 0 when m was -inf
+    m = raise ? mt : m;
     const float m_use = (m == -INFINITY) ? 0.f : m;  // nothing visible yet: weights are 0
-
-    bf16x8 pb[BC / 16];
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -239,26 +266,95 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
         lsum += e;
         pb[2 * kb + (i >> 3)][i & 7] = (__bf16)e;  // round to nearest even
       }
-    l += lsum;
-
-    // O^T += V_j^T P^T; the V^T operand comes from two transpose reads per 16-key step.
+    l = l * alpha + lsum;
+    if (__any(raise)) {
 #pragma unroll
-    for (int kc = 0; kc < BC / 16; ++kc)
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+  };
+  // O^T += V_j^T P^T; the V^T operand comes from two transpose reads per 16-key step.
+  const int trG = (lane >> 4) & 1;  // which 16 of the 32 output dims
+  const int trj = lane & 15;
+  // The V^T fragment of (16-key step kc, 32-dim block db): two transpose reads.
+  auto vfrag = [&](const char* Vs, int kc, int db) {
+    bf16x4 half[2];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        bf16x4 half[2];
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * kc + 8 * h + 4 * g + (trj >> 2);
+      const int cbyte = 64 * db + 32 * trG + 8 * (trj & 3);
+      const int addr = r * C::ROWB + swz_v<C::CHR>(r, cbyte >> 4) * 16 + (cbyte & 15);
+      half[h] = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + addr)));
+    }
+    return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // The D/32 accumulators advance together; step kc+1's fragments load during step kc.
+  auto pv = [&](const char* Vs, const bf16x8 (&pb)[BC / 16]) {
+    constexpr int NKC = BC / 16, NDB = D / 32;
+    bf16x8 va[2][NDB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r = 16 * kc + 8 * h + 4 * g + (trj >> 2);
-          const int cbyte = 64 * db + 32 * trG + 8 * (trj & 3);
-          const int addr = r * C::ROWB + swz_v<C::CHR>(r, cbyte >> 4) * 16 + (cbyte & 15);
-          half[h] = __builtin_bit_cast(
-              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + addr)));
-        }
-        const bf16x8 va = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kc], oacc[db], 0, 0, 0);
+    for (int db = 0; db < NDB; ++db) va[0][db] = vfrag(Vs, 0, db);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      if (kc + 1 < NKC) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) va[(kc + 1) & 1][db] = vfrag(Vs, kc + 1, db);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this step's MFMAs
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kc & 1][db], pb[kc], oacc[db], 0, 0, 0);
+    }
+  };
+
+  // Prologue: tile 0 lands in K and V buffer 0; every wave computes S and the softmax of
+  // tile 0; group 0 starts loading K_1.
+  bf16x8 pb[BC / 16];
+  f32x16 s[BC / 32];
+  if (ntiles > 0 && loader) {
+    issue(kh, koff, 0, kbuf(0));
+    issue(vh, voff, 0, vbuf(0));
   }
+  // Q and tile 0 have landed. Waiting on every path with the builtin lets the compiler see
+  // that the Q loads are complete, so it does not re-wait for them inside the loop (where
+  // the wait would also stall on the in-flight tile loads that share the counter).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unchanged
+  if (ntiles > 0) {
+    wg_barrier();
+    if (loader && ntiles > 1) issue(kh, koff, 1, kbuf(1));
+    if (wave_kv_end > 0) {
+      compute_s(kbuf(0), s);
+      if (needs_mask(0)) mask_s(0, s);
+      softmax(s, pb);
+    }
+    if (!loader) wg_barrier();  // group 1 runs one phase behind group 0
+  }
+
+  // Step j: matrix phase (S for tile j+1 from K_{j+1}, then O += P_j V_j), a barrier, then
+  // the vector phase (softmax of tile j+1, rescale of O). Barriers alternate between the
+  // groups' phases, so one group's matrix phase overlaps the other's vector phase. Group 0
+  // waits for its own loads before its matrix-phase barrier; the loads it issues after that
+  // barrier (K_{j+2}, V_{j+1}) go into the buffers of K_j and V_{j-1}, which both groups
+  // finished reading in the previous step.
+  for (int j = 0; j < ntiles; ++j) {
+    if (loader) wait_loads();
+    wg_barrier();
+    if (loader) {
+      if (j + 2 < ntiles) issue(kh, koff, j + 2, kbuf(j & 1));
+      if (j + 1 < ntiles) issue(vh, voff, j + 1, vbuf((j + 1) & 1));
+    }
+    const bool active = j * BC < wave_kv_end;
+    if (active) {
+      compute_s(kbuf((j + 1) & 1), s);  // past the last tile: stale data, masked out below
+      pv(vbuf(j & 1), pb);
+    }
+    wg_barrier();
+    if (active) {
+      if (needs_mask(j + 1)) mask_s(j + 1, s);
+      softmax(s, pb);
+    }
+  }
+  if (loader && ntiles > 0) wg_barrier();  // match group 1's extra barrier
 
   // Epilogue: divide by l once; LSE = ln2 * (m + log2 l). Empty row: O = 0, LSE = -inf.
   const float lt = wave_half_sum(l);
@@ -281,24 +377,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BC, int NW>
+template <int D, int BC>
 hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
   FwdParams p = prm;
   const int total = p.BH * p.nqt;
   if (causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, true>), dim3(total), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true>), dim3(total), dim3(64 * kNW), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, false>), dim3(total), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false>), dim3(total), dim3(64 * kNW), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int fwd_bf16_block_rows(int) { return 32 * 4; }
+int fwd_bf16_block_rows(int) { return 32 * kNW; }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s) {
-  if (d == 128) return launch<128, 64, 4>(p, causal, s);
-  return launch<64, 128, 4>(p, causal, s);
+  if (d == 128) return launch<128, 64>(p, causal, s);
+  return launch<64, 128>(p, causal, s);
 }
 
 }  // namespace fa
