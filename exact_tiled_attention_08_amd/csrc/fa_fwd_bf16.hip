@@ -179,15 +179,18 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // Rows past Nk re-read row Nk-1.
   auto issue = [&](const uint16_t* base, uint32_t off, int t, char* dst) {
     const int kv0 = t * BC;
-    const bool tail = kv0 + BC > p.Nk;
+    if (kv0 + BC <= p.Nk) {
 #pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) {
-      const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * w) * 16));
-      if (!tail) {
+      for (int n = 0; n < C::LOADS; ++n) {
         // uniform base of this slot row group + the thread's fixed in-group offset
+        const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * w) * 16));
         dma16((const char*)base + (size_t)(kv0 + n * C::ROWSTEP) * C::ROWB, off, lds);
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < C::LOADS; ++n) {
         // tail tile: offset of the clamped row from the head base (< 2^31 bytes)
+        const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * w) * 16));
         const int row = min(kv0 + lrow + n * C::ROWSTEP, p.Nk - 1);
         dma16(base, (uint32_t)(row * C::ROWB) + (off - (uint32_t)(lrow * C::ROWB)), lds);
       }
@@ -336,23 +339,28 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // waits for its own loads before its matrix-phase barrier; the loads it issues after that
   // barrier (K_{j+2}, V_{j+1}) go into the buffers of K_j and V_{j-1}, which both groups
   // finished reading in the previous step.
-  for (int j = 0; j < ntiles; ++j) {
+  auto step = [&](int j, int cur) {  // cur = j & 1, passed as a constant by the unrolled loop
     if (loader) wait_loads();
     wg_barrier();
     if (loader) {
-      if (j + 2 < ntiles) issue(kh, koff, j + 2, kbuf(j & 1));
-      if (j + 1 < ntiles) issue(vh, voff, j + 1, vbuf((j + 1) & 1));
+      if (j + 2 < ntiles) issue(kh, koff, j + 2, kbuf(cur));
+      if (j + 1 < ntiles) issue(vh, voff, j + 1, vbuf(cur ^ 1));
     }
     const bool active = j * BC < wave_kv_end;
     if (active) {
-      compute_s(kbuf((j + 1) & 1), s);  // past the last tile: stale data, masked out below
-      pv(vbuf(j & 1), pb);
+      compute_s(kbuf(cur ^ 1), s);  // past the last tile: stale data, masked out below
+      pv(vbuf(cur), pb);
     }
     wg_barrier();
     if (active) {
       if (needs_mask(j + 1)) mask_s(j + 1, s);
       softmax(s, pb);
     }
+  };
+  // unrolled by two so that every LDS buffer address is a compile-time offset
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < ntiles) step(j + 1, 1);
   }
   if (loader && ntiles > 0) wg_barrier();  // match group 1's extra barrier
 
