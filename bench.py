@@ -16,7 +16,6 @@ sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,20 +30,6 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak (prefill); HBM GB/s (decode)"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = {
-    "fwd_bf16": ["exact_tiled_attention_08_amd/csrc/fa_fwd_bf16.hip",
-                 "exact_tiled_attention_08_amd/csrc/fa_internal.h"],
-    "decode": ["exact_tiled_attention_08_amd/csrc/fa_decode.hip",
-               "exact_tiled_attention_08_amd/csrc/fa_internal.h"],
-}
-
-
-def source_hash(kind: str) -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def traffic_for(kind: str, workload: int):
@@ -55,6 +40,7 @@ def traffic_for(kind: str, workload: int):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
+    from exact_tiled_attention_08_amd.provenance import source_hash
     ent = rec.get(f"{kind}:{workload}")
     if not ent or ent.get("source_hash") != source_hash(kind):
         return None

@@ -1,0 +1,26 @@
+"""Identity of the kernel sources a measurement was taken with.
+
+A stored counter measurement is valid only for the kernel source it was taken on; the
+hash below changes whenever that source changes, and consumers then treat the stored
+figure as absent.
+"""
+from __future__ import annotations
+
+import hashlib
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+KERNEL_SOURCES = {
+    "fwd_bf16": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
+    "fwd_f32": ["csrc/fa_fwd_f32.hip", "csrc/fa_internal.h"],
+    "decode": ["csrc/fa_decode.hip", "csrc/fa_internal.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]

@@ -1,9 +1,18 @@
-"""Summarise a rocprofv3 results database (rocpd SQLite) of this library's kernels.
+"""Summarise rocprofv3 results databases (rocpd SQLite) of this library's kernels.
 
     python -m exact_tiled_attention_08_amd.rocprof_summary DB [DB ...] --command "..." [--match fa::]
 
-Prints a short Markdown report: per-kernel dispatch counts and durations (kernel trace),
+prints a short Markdown report: per-kernel dispatch counts and durations (kernel trace),
 and per-dispatch counter values when the run collected PMC counters (--pmc).
+
+    python -m exact_tiled_attention_08_amd.rocprof_summary traffic --kind fwd_bf16 --workload 3 \
+        --kernel-fetch F.db --kernel-write W.db --copy-fetch CF.db --copy-write CW.db \
+        --match fwd_bf16 --out profiles/hbm_traffic.json
+
+turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a kernel into HBM bytes per launch,
+scaling each counter by the factor that makes it read exactly 2^30 bytes for a plain
+1 GiB device copy measured the same way, and records the result with the hash of the
+kernel source it was taken on.
 """
 from __future__ import annotations
 
@@ -39,14 +48,17 @@ def counter_rows(db: str):
     return [dict(zip(cols, r)) for r in rows]
 
 
-def summarise(dbs, match: str | None):
+def summarise(dbs, match: str | None, wgs: int | None = None):
     by = {}
     for db in dbs:
         for name, dur, grid, wg, lds, vgpr, agpr, _ in kernel_rows(db):
             if match and match not in name:
                 continue
-            ent = by.setdefault(_short(name), {"d": [], "grid": grid, "wg": wg, "lds": lds,
-                                               "vgpr": vgpr, "agpr": agpr})
+            if wgs is not None and grid // max(1, wg) != wgs:
+                continue
+            key = (_short(name), grid // max(1, wg))  # one row per kernel and launch shape
+            ent = by.setdefault(key, {"d": [], "grid": grid, "wg": wg, "lds": lds,
+                                      "vgpr": vgpr, "agpr": agpr})
             ent["d"].append(dur)
     counters = {}
     for db in dbs:
@@ -65,9 +77,10 @@ def summarise(dbs, match: str | None):
 def render(by, counters, command: str) -> str:
     out = ["# rocprofv3 summary", "", "Command:", "", "```", command, "```", ""]
     if by:
-        out += ["| kernel | calls | avg us | min us | max us | grid (WGs) | WG size | LDS B | VGPR | AGPR |",
+        out += ["| kernel | calls | avg us | min us | max us | grid (WGs) | WG size | LDS B | "
+                "VGPR (as reported) | AGPR |",
                 "|---|---|---|---|---|---|---|---|---|---|"]
-        for name, e in sorted(by.items(), key=lambda kv: -sum(kv[1]["d"])):
+        for (name, _), e in sorted(by.items(), key=lambda kv: -sum(kv[1]["d"])):
             d = e["d"]
             out.append(f"| `{name}` | {len(d)} | {statistics.mean(d) / 1e3:.2f} | {min(d) / 1e3:.2f} | "
                        f"{max(d) / 1e3:.2f} | {e['grid'] // max(1, e['wg'])} | {e['wg']} | {e['lds']} | "
@@ -82,13 +95,61 @@ def render(by, counters, command: str) -> str:
     return "\n".join(out)
 
 
+def _counter_mean(db: str, match: str, counter: str) -> float:
+    _, counters = summarise([db], match)
+    vals = [v for (name, c), vs in counters.items() if c == counter for v in vs]
+    if not vals:
+        raise SystemExit(f"no {counter} values for kernels matching {match!r} in {db}")
+    return statistics.mean(vals)
+
+
+def traffic_main(argv):
+    import json
+    import os
+    from exact_tiled_attention_08_amd.provenance import source_hash
+    ap = argparse.ArgumentParser(prog="rocprof_summary traffic")
+    ap.add_argument("--kind", required=True)
+    ap.add_argument("--workload", type=int, required=True)
+    ap.add_argument("--match", required=True)
+    ap.add_argument("--kernel-fetch", required=True)
+    ap.add_argument("--kernel-write", required=True)
+    ap.add_argument("--copy-fetch", required=True)
+    ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--copy-match", default="copyBuffer")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    copy_bytes = float(1 << 30)
+    f_copy = _counter_mean(a.copy_fetch, a.copy_match, "FETCH_SIZE") * 1024.0
+    w_copy = _counter_mean(a.copy_write, a.copy_match, "WRITE_SIZE") * 1024.0
+    fetch_factor, write_factor = copy_bytes / f_copy, copy_bytes / w_copy
+    f = _counter_mean(a.kernel_fetch, a.match, "FETCH_SIZE") * 1024.0 * fetch_factor
+    w = _counter_mean(a.kernel_write, a.match, "WRITE_SIZE") * 1024.0 * write_factor
+    rec = {}
+    if os.path.exists(a.out):
+        with open(a.out) as fh:
+            rec = json.load(fh)
+    rec[f"{a.kind}:{a.workload}"] = {
+        "bytes_per_launch": f + w, "read_bytes": f, "write_bytes": w,
+        "fetch_factor": fetch_factor, "write_factor": write_factor,
+        "source_hash": source_hash(a.kind), "command": a.command}
+    with open(a.out, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec[f"{a.kind}:{a.workload}"], indent=1))
+
+
 def main():
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "traffic":
+        traffic_main(sys.argv[2:])
+        return
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("dbs", nargs="+")
     ap.add_argument("--command", required=True, help="the command that produced the database")
     ap.add_argument("--match", default=None, help="keep kernels whose name contains this")
+    ap.add_argument("--wgs", type=int, default=None, help="keep launches of this many workgroups")
     args = ap.parse_args()
-    by, counters = summarise(args.dbs, args.match)
+    by, counters = summarise(args.dbs, args.match, args.wgs)
     print(render(by, counters, args.command))
 
 
