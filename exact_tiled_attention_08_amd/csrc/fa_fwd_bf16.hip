@@ -205,24 +205,19 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     return *(const bf16x8*)(Ks + r * C::ROWB + swz_k<C::CHR>(r, 2 * kk + g) * 16);
   };
   auto compute_s = [&](const char* Ks, f32x16 (&s)[BC / 32]) {
-    constexpr int NKB = BC / 32, NKK = D / 16, DIST = 2;
-    bf16x8 ka[DIST + 1][NKB];
+    // MFMA number f = kk*NKB + kb; its K fragment is read RING-1 MFMAs ahead
+    constexpr int NKB = BC / 32, NF = NKB * (D / 16), RING = 4;
+    bf16x8 ka[RING];
 #pragma unroll
-    for (int kk = 0; kk < DIST; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) ka[kk][kb] = kfrag(Ks, kb, kk);
+    for (int f = 0; f < RING - 1; ++f) ka[f] = kfrag(Ks, f % NKB, f / NKB);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (kk + DIST < NKK) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) ka[(kk + DIST) % (DIST + 1)][kb] = kfrag(Ks, kb, kk + DIST);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this step's MFMAs
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (DIST + 1)][kb], qb[kk], s[kb], 0, 0, 0);
+    for (int f = 0; f < NF; ++f) {
+      const int fn = f + RING - 1;
+      if (fn < NF) ka[fn % RING] = kfrag(Ks, fn % NKB, fn / NKB);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this MFMA
+      s[f % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[f % RING], qb[f / NKB], s[f % NKB], 0, 0, 0);
     }
   };
   // Mask on absolute positions, only for tiles that cross the key tail or the diagonal
@@ -293,20 +288,17 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   };
   // The D/32 accumulators advance together; step kc+1's fragments load during step kc.
   auto pv = [&](const char* Vs, const bf16x8 (&pb)[BC / 16]) {
-    constexpr int NKC = BC / 16, NDB = D / 32;
-    bf16x8 va[2][NDB];
+    // MFMA number f = kc*NDB + db; its V^T fragment is read RING-1 MFMAs ahead
+    constexpr int NDB = D / 32, NF = NDB * (BC / 16), RING = 4;
+    bf16x8 va[RING];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) va[0][db] = vfrag(Vs, 0, db);
+    for (int f = 0; f < RING - 1; ++f) va[f] = vfrag(Vs, f / NDB, f % NDB);
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      if (kc + 1 < NKC) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) va[(kc + 1) & 1][db] = vfrag(Vs, kc + 1, db);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this step's MFMAs
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kc & 1][db], pb[kc], oacc[db], 0, 0, 0);
+    for (int f = 0; f < NF; ++f) {
+      const int fn = f + RING - 1;
+      if (fn < NF) va[fn % RING] = vfrag(Vs, fn / NDB, fn % NDB);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this MFMA
+      oacc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[f % RING], pb[f / NDB], oacc[f % NDB], 0, 0, 0);
     }
   };
 
@@ -348,8 +340,9 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     }
     const bool active = j * BC < wave_kv_end;
     if (active) {
-      compute_s(kbuf(cur ^ 1), s);  // past the last tile: stale data, masked out below
+      // PV first: P_j dies before S_{j+1} is born, so the two never hold registers together
       pv(vbuf(cur), pb);
+      compute_s(kbuf(cur ^ 1), s);  // past the last tile: stale data, masked out below
     }
     wg_barrier();
     if (active) {
@@ -401,7 +394,7 @@ hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
 int fwd_bf16_block_rows(int) { return 32 * kNW; }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s) {
-  if (d == 128) return launch<128, 64>(p, causal, s);
+  if (d == 128) return launch<128, 96>(p, causal, s);
   return launch<64, 128>(p, causal, s);
 }
 
