@@ -32,8 +32,8 @@
 // alternates a matrix phase (S for the next tile and PV for the current tile, all MFMA)
 // with a vector phase (mask, online softmax, rescale of O), and the groups run half a
 // step apart, separated by workgroup barriers: while one group's waves keep a SIMD's
-// matrix core busy, the other group's waves use its vector ALU. Group 0 also issues the
-// direct loads of the next K and V tiles, two phases ahead of their first use.
+// matrix core busy, the other group's waves use its vector ALU. Group 0 issues the direct
+// loads of K tiles and group 1 those of V tiles, each two phases ahead of the first use.
 //
 // Rescaling: the offset is always the exact running max, so the largest weight of a row
 // is exactly 1 and survives the rounding of P to bfloat16 without error (an offset that
@@ -55,13 +55,13 @@ template <int D, int BC>
 struct Cfg {
   static constexpr int BR = 32 * kNW;         // query rows per workgroup
   static constexpr int T = 64 * kNW;          // threads per workgroup
-  static constexpr int TL = T / 2;            // threads that issue loads (group 0)
+  static constexpr int TL = T / 2;            // threads that load one tensor (one group)
   static constexpr int ROWB = D * 2;          // bytes per K or V row in LDS (unpadded)
   static constexpr int CHR = D / 8;           // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;     // bytes of one K (or V) tile
   static constexpr int LDS = 4 * TILEB;       // two K buffers, two V buffers
   static constexpr int SLOTS = BC * CHR;      // 16-byte slots per tile
-  static constexpr int LOADS = SLOTS / TL;    // direct loads per loading thread per tile
+  static constexpr int LOADS = SLOTS / TL;    // direct loads per thread per tile
   static constexpr int ROWSTEP = TL / CHR;    // rows between a thread's successive slots
   static_assert(D % 32 == 0 && BC % 32 == 0 && CHR >= 8, "tile shape");
   static_assert(SLOTS % TL == 0 && TL % CHR == 0, "slots must split evenly over threads");
@@ -175,50 +175,29 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   const uint32_t voff = (uint32_t)(lrow * C::ROWB + 16 * swz_v<C::CHR>(lrow, lpos));
   auto kbuf = [&](int i) -> char* { return smem + i * C::TILEB; };
   auto vbuf = [&](int i) -> char* { return smem + (2 + i) * C::TILEB; };
-  // Issue the direct loads of one tile of K (or V) into an LDS buffer (loading group only).
-  // Rows past Nk re-read row Nk-1.
-  auto issue = [&](const uint16_t* base, uint32_t off, int t, char* dst) {
+  // Group 0 loads the K tiles and group 1 the V tiles. One direct load (slot group n of
+  // tile t) of this wave into LDS buffer dst: key rows past Nk re-read row Nk-1, so the
+  // per-lane offset is the clamped row's (< 2^31 bytes: Nk * d <= 2^30) plus the lane's
+  // swizzled chunk within the row, against the tile's 64-bit base.
+  const uint16_t* const lbase = loader ? kh : vh;
+  const uint32_t lchunk = (loader ? koff : voff) - (uint32_t)(lrow * C::ROWB);
+  const int wg4 = w & 3;  // wave index within its group
+  auto dma = [&](int t, char* dst, int n) {
     const int kv0 = t * BC;
-    if (kv0 + BC <= p.Nk) {
+    const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * wg4) * 16));
+    const int row = min(lrow + n * C::ROWSTEP, p.Nk - 1 - kv0);
+    dma16((const char*)lbase + (size_t)kv0 * C::ROWB, (uint32_t)(row * C::ROWB) + lchunk, lds);
+  };
+  auto issue = [&](int t, char* dst) {
 #pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) {
-        // uniform base of this slot row group + the thread's fixed in-group offset
-        const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * w) * 16));
-        dma16((const char*)base + (size_t)(kv0 + n * C::ROWSTEP) * C::ROWB, off, lds);
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < C::LOADS; ++n) {
-        // tail tile: offset of the clamped row from the head base (< 2^31 bytes)
-        const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * w) * 16));
-        const int row = min(kv0 + lrow + n * C::ROWSTEP, p.Nk - 1);
-        dma16(base, (uint32_t)(row * C::ROWB) + (off - (uint32_t)(lrow * C::ROWB)), lds);
-      }
-    }
+    for (int n = 0; n < C::LOADS; ++n) dma(t, dst, n);
   };
 
-  // S^T tile = K_j Q_i^T  (BC keys x 32 queries per wave). The BC/32 accumulators advance
-  // together along the contraction (consecutive MFMAs are independent), and the K
-  // fragments of step kk+2 are read from LDS while step kk's MFMAs run.
+  // K fragment (A operand of S^T = K_j Q_i^T, BC keys x 32 queries per wave) of key block
+  // kb and 16-dim contraction step kk.
   auto kfrag = [&](const char* Ks, int kb, int kk) {
     const int r = 32 * kb + col;
     return *(const bf16x8*)(Ks + r * C::ROWB + swz_k<C::CHR>(r, 2 * kk + g) * 16);
-  };
-  auto compute_s = [&](const char* Ks, f32x16 (&s)[BC / 32]) {
-    // MFMA number f = kk*NKB + kb; its K fragment is read RING-1 MFMAs ahead
-    constexpr int NKB = BC / 32, NF = NKB * (D / 16), RING = 4;
-    bf16x8 ka[RING];
-#pragma unroll
-    for (int f = 0; f < RING - 1; ++f) ka[f] = kfrag(Ks, f % NKB, f / NKB);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int fn = f + RING - 1;
-      if (fn < NF) ka[fn % RING] = kfrag(Ks, fn % NKB, fn / NKB);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this MFMA
-      s[f % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[f % RING], qb[f / NKB], s[f % NKB], 0, 0, 0);
-    }
   };
   // Mask on absolute positions, only for tiles that cross the key tail or the diagonal
   // (a tile past the wave's keys is masked out entirely):
@@ -286,37 +265,56 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     }
     return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  // The D/32 accumulators advance together; step kc+1's fragments load during step kc.
-  auto pv = [&](const char* Vs, const bf16x8 (&pb)[BC / 16]) {
-    // MFMA number f = kc*NDB + db; its V^T fragment is read RING-1 MFMAs ahead
-    constexpr int NDB = D / 32, NF = NDB * (BC / 16), RING = 4;
-    bf16x8 va[RING];
+  // Matrix phase: O^T += V_j^T P_j^T (MFMAs 0 .. NPV-1), then S^T = K_{j+1} Q^T (MFMAs
+  // NPV .. NF-1, into freshly zeroed accumulators). In each product the accumulators
+  // advance together along the contraction, so consecutive MFMAs are independent; the A
+  // fragment of MFMA f is read from LDS RING-1 MFMAs ahead, across the boundary between
+  // the two products.
+  constexpr int NDB = D / 32, NKB = BC / 32;
+  constexpr int NPV = NDB * (BC / 16), NF = NPV + NKB * (D / 16), RING = 4;
+  auto afrag = [&](const char* Vs, const char* Ks, int f) {
+    return f < NPV ? vfrag(Vs, f / NDB, f % NDB) : kfrag(Ks, (f - NPV) % NKB, (f - NPV) / NKB);
+  };
+  auto matrix = [&](const char* Vs, const char* Ks, const bf16x8 (&pb)[BC / 16],
+                    f32x16 (&s)[BC / 32]) {
+    bf16x8 fr[RING];
 #pragma unroll
-    for (int f = 0; f < RING - 1; ++f) va[f] = vfrag(Vs, f / NDB, f % NDB);
+    for (int f = 0; f < RING - 1; ++f) fr[f] = afrag(Vs, Ks, f);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int fn = f + RING - 1;
-      if (fn < NF) va[fn % RING] = vfrag(Vs, fn / NDB, fn % NDB);
+      if (fn < NF) fr[fn % RING] = afrag(Vs, Ks, fn);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this MFMA
-      oacc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[f % RING], pb[f / NDB], oacc[f % NDB], 0, 0, 0);
+      if (f < NPV) {
+        oacc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], pb[f / NDB], oacc[f % NDB], 0, 0, 0);
+      } else {
+        const int g2 = f - NPV;
+        s[g2 % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fr[f % RING], qb[g2 / NKB], g2 < NKB ? f32x16{} : s[g2 % NKB], 0, 0, 0);
+      }
     }
   };
+  // Prologue only: S^T of tile 0.
+  auto compute_s = [&](const char* Ks, f32x16 (&s)[BC / 32]) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(Ks, kb, kk), qb[kk], kk == 0 ? f32x16{} : s[kb], 0, 0, 0);
+  };
 
-  // Prologue: tile 0 lands in K and V buffer 0; every wave computes S and the softmax of
-  // tile 0; group 0 starts loading K_1.
+  // Prologue: tile 0 lands in K and V buffer 0 (group 0 loads K, group 1 loads V); every
+  // wave computes S and the softmax of tile 0; each group starts loading its tile 1.
   bf16x8 pb[BC / 16];
   f32x16 s[BC / 32];
-  if (ntiles > 0 && loader) {
-    issue(kh, koff, 0, kbuf(0));
-    issue(vh, voff, 0, vbuf(0));
-  }
+  if (ntiles > 0) issue(0, loader ? kbuf(0) : vbuf(0));
   // Q and tile 0 have landed. Waiting on every path with the builtin lets the compiler see
   // that the Q loads are complete, so it does not re-wait for them inside the loop (where
   // the wait would also stall on the in-flight tile loads that share the counter).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unchanged
   if (ntiles > 0) {
     wg_barrier();
-    if (loader && ntiles > 1) issue(kh, koff, 1, kbuf(1));
+    if (ntiles > 1) issue(1, loader ? kbuf(1) : vbuf(1));
     if (wave_kv_end > 0) {
       compute_s(kbuf(0), s);
       if (needs_mask(0)) mask_s(0, s);
@@ -325,30 +323,29 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     if (!loader) wg_barrier();  // group 1 runs one phase behind group 0
   }
 
-  // Step j: matrix phase (S for tile j+1 from K_{j+1}, then O += P_j V_j), a barrier, then
-  // the vector phase (softmax of tile j+1, rescale of O). Barriers alternate between the
-  // groups' phases, so one group's matrix phase overlaps the other's vector phase. Group 0
-  // waits for its own loads before its matrix-phase barrier; the loads it issues after that
-  // barrier (K_{j+2}, V_{j+1}) go into the buffers of K_j and V_{j-1}, which both groups
-  // finished reading in the previous step.
+  // Step j: matrix phase (O += P_j V_j, then S for tile j+1 from K_{j+1}), a barrier, then
+  // the vector phase (mask and softmax of tile j+1, rescale of O). Barriers alternate
+  // between the groups' phases, so one group's matrix phase overlaps the other's vector
+  // phase. Both groups issue their next loads in the same interval between two barriers:
+  // group 0 loads K_{j+2} at the start of its matrix phase of step j, group 1 loads
+  // V_{j+2} at the end of its vector phase of step j, which runs alongside group 0's
+  // matrix phase of step j+1. Each goes into the buffer of tile j, which both groups
+  // finished reading before that interval, and each group waits for its loads at the last
+  // barrier before the first reader: group 0 before its step j+1 matrix phase, group 1
+  // before its mid-step barrier of step j+1.
   auto step = [&](int j, int cur) {  // cur = j & 1, passed as a constant by the unrolled loop
-    if (loader) wait_loads();
+    if (loader) wait_loads();  // K_{j+1}
     wg_barrier();
-    if (loader) {
-      if (j + 2 < ntiles) issue(kh, koff, j + 2, kbuf(cur));
-      if (j + 1 < ntiles) issue(vh, voff, j + 1, vbuf(cur ^ 1));
-    }
+    if (loader && j + 2 < ntiles) issue(j + 2, kbuf(cur));
     const bool active = j * BC < wave_kv_end;
-    if (active) {
-      // PV first: P_j dies before S_{j+1} is born, so the two never hold registers together
-      pv(vbuf(cur), pb);
-      compute_s(kbuf(cur ^ 1), s);  // past the last tile: stale data, masked out below
-    }
+    if (active) matrix(vbuf(cur), kbuf(cur ^ 1), pb, s);  // past the last tile, S is stale
+    if (!loader) wait_loads();                            // and masked out below; V_{j+1}
     wg_barrier();
     if (active) {
       if (needs_mask(j + 1)) mask_s(j + 1, s);
       softmax(s, pb);
     }
+    if (!loader && j + 2 < ntiles) issue(j + 2, vbuf(cur));
   };
   // unrolled by two so that every LDS buffer address is a compile-time offset
   for (int j = 0; j < ntiles; j += 2) {
