@@ -13,6 +13,14 @@ turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a kernel into HBM bytes per 
 scaling each counter by the factor that makes it read exactly 2^30 bytes for a plain
 1 GiB device copy measured the same way, and records the result with the hash of the
 kernel source it was taken on.
+
+    python -m exact_tiled_attention_08_amd.rocprof_summary mfma DB --match fwd_bf16 --wgs 1024 \
+        --workload 3 --command "..."
+
+reports the matrix-core counters of a --pmc run (MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE): the MFMA busy fraction, the
+bf16 MFMA FLOPs the hardware counted (MOPS x 512) next to the algorithmic FLOPs of the
+workload, and both as rates over the kernel's average duration in the same run.
 """
 from __future__ import annotations
 
@@ -138,10 +146,57 @@ def traffic_main(argv):
     print(json.dumps(rec[f"{a.kind}:{a.workload}"], indent=1))
 
 
+def mfma_main(argv):
+    import os
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import workloads as W
+    ap = argparse.ArgumentParser(prog="rocprof_summary mfma")
+    ap.add_argument("db")
+    ap.add_argument("--match", required=True)
+    ap.add_argument("--wgs", type=int, default=None)
+    ap.add_argument("--workload", type=int, required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--peak-tflops", type=float, default=2516.6)
+    a = ap.parse_args(argv)
+    by, counters = summarise([a.db], a.match, a.wgs)
+    print(render(by, counters, a.command))
+    if len(by) != 1:
+        raise SystemExit(f"expected one kernel launch shape, found {len(by)}")
+    (name, _), ent = next(iter(by.items()))
+    dur_s = statistics.mean(ent["d"]) * 1e-9
+
+    def mean(c):
+        vals = [v for (n, cn), vs in counters.items() if cn == c for v in vs]
+        return statistics.mean(vals) if vals else None
+
+    w = W.WORKLOADS[a.workload]
+    mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    util = mean("MfmaUtil")
+    out = ["| derived | value |", "|---|---|"]
+    if util is not None:
+        out.append(f"| MFMA busy (MfmaUtil: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs)) | {util:.1f}% |")
+    if mops is not None:
+        hw = mops * 512.0
+        out.append(f"| bf16 MFMA FLOPs counted per dispatch (MOPS x 512) | {hw:.4g} |")
+        out.append(f"| algorithmic FLOPs per launch ({w.name}) | {w.flops:.4g} |")
+        out.append(f"| counted / algorithmic | {hw / w.flops:.4f} |")
+        out.append(f"| counted MFMA rate over the average duration | {hw / dur_s / 1e12:.1f} TFLOP/s "
+                   f"({100 * hw / dur_s / 1e12 / a.peak_tflops:.1f}% of {a.peak_tflops}) |")
+    out.append(f"| algorithmic rate over the average duration ({statistics.mean(ent['d']) / 1e3:.1f} us) | "
+               f"{w.flops / dur_s / 1e12:.1f} TFLOP/s ({100 * w.flops / dur_s / 1e12 / a.peak_tflops:.1f}%) |")
+    print("\n".join(out))
+
+
 def main():
     import sys
     if len(sys.argv) > 1 and sys.argv[1] == "traffic":
         traffic_main(sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "mfma":
+        mfma_main(sys.argv[2:])
         return
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("dbs", nargs="+")
