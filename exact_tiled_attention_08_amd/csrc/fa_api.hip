@@ -9,7 +9,6 @@
 namespace {
 
 constexpr long long kMaxHeadElems = 1LL << 30;  // Nk * d per head: 32-bit in-head offsets
-constexpr int kMaxSplits = 1024;
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -101,7 +100,7 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
   if (BH * num_splits > INT32_MAX) return FA_ERR_SHAPE;
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if ((long long)Nk * d > kMaxHeadElems || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || num_splits > fa::kMaxSplits) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_VALUE;
   const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
   if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;

@@ -24,7 +24,8 @@ namespace fa {
 namespace {
 
 constexpr int kNT = 256;  // threads per split workgroup
-constexpr int kU = 8;     // keys per lane group per step (loads in flight per thread: 2*kU)
+constexpr int kU = 16;    // keys per lane group per step (loads in flight per thread: 2*kU)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 template <typename E>
 struct Elem;
@@ -85,8 +86,11 @@ __global__ __launch_bounds__(kNT) void decode_split_kernel(DecodeParams p) {
     for (int u = 0; u < kU; ++u) {
       const int key = base + u * KPI + grp;
       if (key < hi) {
-        kx[u] = *(const uint4*)(kh + (size_t)key * D + sub * VEC);
-        vx[u] = *(const uint4*)(vh + (size_t)key * D + sub * VEC);
+        // streamed once: non-temporal loads keep the cache for the workspace and q
+        const v4u a = __builtin_nontemporal_load((const v4u*)(kh + (size_t)key * D + sub * VEC));
+        const v4u b = __builtin_nontemporal_load((const v4u*)(vh + (size_t)key * D + sub * VEC));
+        kx[u] = make_uint4(a[0], a[1], a[2], a[3]);
+        vx[u] = make_uint4(b[0], b[1], b[2], b[3]);
       } else {
         kx[u] = make_uint4(0, 0, 0, 0);
         vx[u] = make_uint4(0, 0, 0, 0);
@@ -161,21 +165,27 @@ __global__ __launch_bounds__(kNT) void decode_split_kernel(DecodeParams p) {
   }
 }
 
+// The S (m, l) pairs of one (b, h) are staged in LDS once; each thread then combines the
+// S partials of its output dimension with independent loads in flight.
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
+  __shared__ float sml[2 * kMaxSplits];
   const int bh = blockIdx.x;
   const int dd = threadIdx.x;
   const float* ml = p.ws_ml + (size_t)bh * p.S * 2;
   const float* os = p.ws_o + (size_t)bh * p.S * D;
+  for (int i = dd; i < 2 * p.S; i += D) sml[i] = ml[i];
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s = 0; s < p.S; ++s) M = fmaxf(M, sml[2 * s]);
   float L = 0.f, O = 0.f;
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < p.S; ++s) {
-      const float ms = ml[2 * s];
-      if (ms == -INFINITY) continue;  // empty chunk
+      const float ms = sml[2 * s];
+      // an empty chunk (m = -inf) gets weight exp2(-inf) = 0 and its o and l are 0
       const float wgt = __builtin_amdgcn_exp2f(ms - M);
-      L = __builtin_fmaf(wgt, ml[2 * s + 1], L);
+      L = __builtin_fmaf(wgt, sml[2 * s + 1], L);
       O = __builtin_fmaf(wgt, os[(size_t)s * D + dd], O);
     }
   }

@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSplits = 1024;  // largest num_splits of the split-KV decode
 
 // Arguments of the prefill kernels (one struct keeps the launch signature small).
 struct FwdParams {
