@@ -21,8 +21,16 @@ fa_status finish_launch(hipError_t e) {
   return FA_ERR_HIP;
 }
 
-// (b, h) pairs handled together on one XCD (see fa::map_block).
-int heads_per_group(int BH) { return (BH % 8 == 0) ? BH / 8 : 1; }
+// (b, h) pairs handled together on one XCD (see fa::map_block). The XCD's CUs walk the
+// group's query tiles together, so each K/V tile is fetched into its L2 once per round of
+// concurrently running tiles of a head; with long sequences (many query tiles) fewer heads
+// per group mean more tiles of one head per round, hence fewer re-reads from HBM
+// (measured: 3% faster at 118 query tiles per head, no gain at 32).
+int heads_per_group(int BH, long long nqt) {
+  if (BH % 8 != 0) return 1;
+  const int per_xcd = BH / 8;
+  return (nqt > 64 && per_xcd % 2 == 0) ? 2 : per_xcd;
+}
 
 }  // namespace
 
@@ -74,7 +82,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
   p.Nk = Nk;
   p.off = Nk - Nq;
   p.nqt = (int)nqt;
-  p.hpg = heads_per_group((int)BH);
+  p.hpg = heads_per_group((int)BH, nqt);
   p.c = scale * fa::kLog2e;
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, d, causal != 0, (hipStream_t)stream)
