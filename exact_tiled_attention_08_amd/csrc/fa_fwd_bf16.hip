@@ -275,15 +275,17 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   auto afrag = [&](const char* Vs, const char* Ks, int f) {
     return f < NPV ? vfrag(Vs, f / NDB, f % NDB) : kfrag(Ks, (f - NPV) % NKB, (f - NPV) / NKB);
   };
-  auto matrix = [&](const char* Vs, const char* Ks, const bf16x8 (&pb)[BC / 16],
-                    f32x16 (&s)[BC / 32]) {
+  // With WITH_S false (the last tile) only the PV MFMAs run.
+  auto matrix = [&]<bool WITH_S>(const char* Vs, const char* Ks, const bf16x8 (&pb)[BC / 16],
+                                 f32x16 (&s)[BC / 32]) {
+    constexpr int NM = WITH_S ? NF : NPV;
     bf16x8 fr[RING];
 #pragma unroll
     for (int f = 0; f < RING - 1; ++f) fr[f] = afrag(Vs, Ks, f);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    for (int f = 0; f < NM; ++f) {
       const int fn = f + RING - 1;
-      if (fn < NF) fr[fn % RING] = afrag(Vs, Ks, fn);
+      if (fn < NM) fr[fn % RING] = afrag(Vs, Ks, fn);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this MFMA
       if (f < NPV) {
         oacc[f % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], pb[f / NDB], oacc[f % NDB], 0, 0, 0);
@@ -323,12 +325,12 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     if (!loader) wg_barrier();  // group 1 runs one phase behind group 0
   }
 
-  // Step j: matrix phase (O += P_j V_j, then S for tile j+1 from K_{j+1}), a barrier, then
-  // the vector phase (mask and softmax of tile j+1, rescale of O). Barriers alternate
-  // between the groups' phases, so one group's matrix phase overlaps the other's vector
-  // phase. Both groups issue their next loads in the same interval between two barriers:
-  // group 0 loads K_{j+2} at the start of its matrix phase of step j, group 1 loads
-  // V_{j+2} at the end of its vector phase of step j, which runs alongside group 0's
+  // Step j < ntiles - 1: matrix phase (O += P_j V_j, then S for tile j+1 from K_{j+1}), a
+  // barrier, then the vector phase (mask and softmax of tile j+1, rescale of O). Barriers
+  // alternate between the groups' phases, so one group's matrix phase overlaps the other's
+  // vector phase. Both groups issue their next loads in the same interval between two
+  // barriers: group 0 loads K_{j+2} at the start of its matrix phase of step j, group 1
+  // loads V_{j+2} at the end of its vector phase of step j, which runs alongside group 0's
   // matrix phase of step j+1. Each goes into the buffer of tile j, which both groups
   // finished reading before that interval, and each group waits for its loads at the last
   // barrier before the first reader: group 0 before its step j+1 matrix phase, group 1
@@ -338,8 +340,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     wg_barrier();
     if (loader && j + 2 < ntiles) issue(j + 2, kbuf(cur));
     const bool active = j * BC < wave_kv_end;
-    if (active) matrix(vbuf(cur), kbuf(cur ^ 1), pb, s);  // past the last tile, S is stale
-    if (!loader) wait_loads();                            // and masked out below; V_{j+1}
+    if (active) matrix.template operator()<true>(vbuf(cur), kbuf(cur ^ 1), pb, s);
+    if (!loader) wait_loads();  // V_{j+1}
     wg_barrier();
     if (active) {
       if (needs_mask(j + 1)) mask_s(j + 1, s);
@@ -347,12 +349,26 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     }
     if (!loader && j + 2 < ntiles) issue(j + 2, vbuf(cur));
   };
-  // unrolled by two so that every LDS buffer address is a compile-time offset
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, 0);
-    if (j + 1 < ntiles) step(j + 1, 1);
+  // Step ntiles - 1: PV of the last tile only (there is no next tile to score). The
+  // barriers keep the same count as a full step, so both groups end the loop together.
+  auto last_step = [&](int j, int cur) {
+    wg_barrier();
+    if (j * BC < wave_kv_end) matrix.template operator()<false>(vbuf(cur), kbuf(cur ^ 1), pb, s);
+    wg_barrier();
+  };
+  if (ntiles > 0) {
+    // steps in pairs so that every LDS buffer address is a compile-time offset
+    const int last = ntiles - 1;
+    for (int j = 0; j < last; j += 2) {
+      step(j, 0);
+      if (j + 1 < last) step(j + 1, 1);
+    }
+    if (last & 1)
+      last_step(last, 1);
+    else
+      last_step(last, 0);
+    if (loader) wg_barrier();  // match group 1's extra barrier
   }
-  if (loader && ntiles > 0) wg_barrier();  // match group 1's extra barrier
 
   // Epilogue: divide by l once; LSE = ln2 * (m + log2 l). Empty row: O = 0, LSE = -inf.
   const float lt = wave_half_sum(l);
