@@ -146,6 +146,35 @@ def traffic_main(argv):
     print(json.dumps(rec[f"{a.kind}:{a.workload}"], indent=1))
 
 
+def kernel_mfma_count(w, br: int = 256, bc: int | None = None) -> int:
+    """Exact number of v_mfma_f32_32x32x16_bf16 the bf16 prefill kernel issues for workload w:
+    per wave (32 query rows of a 256-row workgroup), S of the first key tile in the prologue,
+    PV + S for every further tile the wave sees, PV only for the workgroup's last tile.
+    Compared with SQ_INSTS_VALU_MFMA_MOPS_BF16 it pins what one counted op is."""
+    import math
+    d = w.d
+    bc = bc or (96 if d == 128 else 128)
+    npv, ns = (d // 32) * (bc // 16), (bc // 32) * (d // 16)
+    off = w.Nk - w.Nq
+    total = 0
+    for qt in range(math.ceil(w.Nq / br)):
+        q0 = qt * br
+        kv_end = min(w.Nk, min(q0 + br, w.Nq) - 1 + off + 1) if w.causal else w.Nk
+        nt = math.ceil(kv_end / bc) if kv_end > 0 else 0
+        for wv in range(br // 32):
+            wq0 = q0 + 32 * wv
+            if wq0 >= w.Nq or nt == 0:
+                continue
+            wkv = min(w.Nk, min(wq0 + 31, w.Nq - 1) + off + 1) if w.causal else w.Nk
+            if wkv <= 0:
+                continue
+            c = ns
+            c += sum(npv + ns for j in range(nt - 1) if j * bc < wkv)
+            c += npv if (nt - 1) * bc < wkv else 0
+            total += c
+    return total * w.B * w.H
+
+
 def mfma_main(argv):
     import os
     import sys
@@ -183,6 +212,10 @@ def mfma_main(argv):
         out.append(f"| bf16 MFMA FLOPs counted per dispatch (MOPS x 512) | {hw:.4g} |")
         out.append(f"| algorithmic FLOPs per launch ({w.name}) | {w.flops:.4g} |")
         out.append(f"| counted / algorithmic | {hw / w.flops:.4f} |")
+        n = kernel_mfma_count(w)
+        out.append(f"| 32x32x16 MFMAs the kernel issues (from its loop structure) | {n} |")
+        out.append(f"| counted MOPS / (64 x issued MFMAs): 1 means one MOP = 512 FLOP | "
+                   f"{mops / (64.0 * n):.6f} |")
         out.append(f"| counted MFMA rate over the average duration | {hw / dur_s / 1e12:.1f} TFLOP/s "
                    f"({100 * hw / dur_s / 1e12 / a.peak_tflops:.1f}% of {a.peak_tflops}) |")
     out.append(f"| algorithmic rate over the average duration ({statistics.mean(ent['d']) / 1e3:.1f} us) | "
