@@ -6,7 +6,9 @@ links or calls it, and it imports nothing from the HIP library: the two share
 only the seeded input generators in ``workloads.py``.
 
 ``attention`` evaluates the plain definition O = softmax(Q K^T * scale + mask) V
-row by row in double precision (the C source states each passage it follows).
+row by row in double precision (the C source states each passage it follows);
+``attention_bwd`` evaluates the gradients of sum(O * dO) with respect to Q, K, V
+from the same definition by the chain rule.
 """
 from __future__ import annotations
 
@@ -46,6 +48,13 @@ def load_library(path: str):
                   ctypes.c_double, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    g = lib.oracle_attention_bwd
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_double, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -128,3 +137,48 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
     return (o, lse, p) if want_p else (o, lse)
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool = False, qrows=None, krows=None,
+                  threads: int | None = None):
+    """Float64 gradients of sum(O * dO) for O = attention(q, k, v).
+
+    q, do [B,H,Nq,d]; k, v [B,H,Nk,d]; all float32 or all bfloat16.
+    ``qrows``: flat query rows (b*H + h)*Nq + i whose dQ is returned (default all);
+    ``krows``: flat key rows (b*H + h)*Nk + j whose dK and dV are returned (default all).
+    Returns (dq [nq, d], dk [nk, d], dv [nk, d]) float64.
+    """
+    qa, dt = _as_input(q)
+    ka, dtk = _as_input(k)
+    va, dtv = _as_input(v)
+    da, dtd = _as_input(do)
+    if not (dt == dtk == dtv == dtd):
+        raise TypeError("q, k, v and do must share one dtype")
+    if qa.ndim != 4 or ka.ndim != 4 or va.ndim != 4 or da.shape != qa.shape:
+        raise ValueError("q, do must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    B, H, Nq, d = qa.shape
+    if ka.shape[:2] != (B, H) or ka.shape[3] != d or va.shape != ka.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    Nk = ka.shape[2]
+
+    def rows_of(rows, total):
+        if rows is None:
+            return None, total
+        arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        return arr, int(arr.size)
+
+    qr, nq = rows_of(qrows, B * H * Nq)
+    kr, nk = rows_of(krows, B * H * Nk)
+    threads = threads or default_threads()
+    dq = np.empty((nq, d), np.float64)
+    dk = np.empty((nk, d), np.float64)
+    dv = np.empty((nk, d), np.float64)
+    rc = _load().oracle_attention_bwd(
+        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, dt, B, H, Nq, Nk, d,
+        float(scale), int(bool(causal)),
+        qr.ctypes.data if qr is not None else None, nq,
+        kr.ctypes.data if kr is not None else None, nk, threads,
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd rejected its arguments")
+    return dq, dk, dv

@@ -7,7 +7,8 @@
  * with the HIP library, and the HIP library never calls it.
  *
  * What it computes is the plain definition, written out with no tiling, no
- * running statistics and no reordering:
+ * running statistics and no reordering (and, further down, the gradients of
+ * that definition for a backward pass):
  *
  *   S = Q K^T * scale (+ mask)      P = softmax(S) row by row      O = P V
  *
@@ -40,6 +41,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_F32 1
@@ -139,5 +141,182 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
             scratch + (size_t)tid * (size_t)Nk, o + (size_t)n * d, lse + n,
             p ? p + (size_t)n * Nk : NULL);
   }
+  return 0;
+}
+
+/*
+ * Backward pass: gradients of the loss sum(O * dO) with respect to Q, K and V,
+ * for the same attention as above. The pages say only that a backward pass
+ * recomputes the probability tiles from the saved per-row statistics instead
+ * of storing P ("Flash Attention Optimization", section "Sizing a tile, and
+ * why the backward pass recomputes instead of storing"; "Explain
+ * FlashAttention ...", section "Exact attention, finite precision and
+ * backward"); the gradients themselves follow from the definition
+ * O = P V, P = softmax(S) row by row, S = scale * Q K^T (+ mask) by the chain
+ * rule, written out here in double precision:
+ *
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - sum_t P_it dP_it)          (softmax Jacobian)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *
+ * with P_ij = exp(s_ij - LSE_i) (the identity exp(s - m) / l = exp(s - (m + ln l)))
+ * and sum_t P_it dP_it = dO_i . O_i. Masked pairs have P = 0 and contribute
+ * nothing; a row with no visible key has P = 0 everywhere.
+ *
+ * Row statistics pass: for every query row of a head, LSE_i and
+ * Dsum_i = dO_i . O_i from the definition above (one_row). dQ rows need only
+ * their own row; dK and dV rows need the statistics of every query row of the
+ * head, which are computed for each head that a requested key row belongs to.
+ */
+static void row_stats(const void* q, const void* k, const void* v, const void* dout,
+                      int dtype, int H, int Nq, int Nk, int d, double scale, int causal,
+                      long long r, double* s, double* o, double* lse, double* dsum) {
+  one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, r, s, o, lse, NULL);
+  double acc = 0.0;
+  for (int t = 0; t < d; ++t) acc += widen(dout, dtype, (size_t)r * d + t) * o[t];
+  *dsum = acc;
+}
+
+/* score of (query row r, key j of the same head) or -inf when masked */
+static double score(const void* q, const void* k, int dtype, int Nq, int Nk, int d,
+                    double scale, int causal, long long r, int j) {
+  long long bh = r / Nq;
+  int i = (int)(r % Nq);
+  if (causal && (long long)j - (long long)(Nk - Nq) > (long long)i) return -INFINITY;
+  size_t qoff = (size_t)r * d, koff = ((size_t)bh * Nk + j) * d;
+  double dot = 0.0;
+  for (int t = 0; t < d; ++t) dot += widen(q, dtype, qoff + t) * widen(k, dtype, koff + t);
+  return scale * dot;
+}
+
+/* dP_ij = dO_i . v_j */
+static double dprob(const void* dout, const void* v, int dtype, int Nq, int Nk, int d,
+                    long long r, int j) {
+  long long bh = r / Nq;
+  size_t ooff = (size_t)r * d, voff = ((size_t)bh * Nk + j) * d;
+  double dot = 0.0;
+  for (int t = 0; t < d; ++t) dot += widen(dout, dtype, ooff + t) * widen(v, dtype, voff + t);
+  return dot;
+}
+
+/*
+ * oracle_attention_bwd
+ *   q [B][H][Nq][d], k, v [B][H][Nk][d], dout [B][H][Nq][d], one dtype.
+ *   qrows : flat query rows (b*H + h)*Nq + i whose dQ is wanted (nq of them),
+ *           or NULL for all;  dq : [nq][d] doubles (may be NULL if nq == 0).
+ *   krows : flat key rows (b*H + h)*Nk + j whose dK and dV are wanted (nk of
+ *           them), or NULL for all;  dk, dv : [nk][d] doubles.
+ *   nthreads : OpenMP threads. Returns 0, or -1 for an invalid argument or a
+ *   failed allocation.
+ */
+int oracle_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
+                         int dtype, int B, int H, int Nq, int Nk, int d, double scale,
+                         int causal, const long long* qrows, long long nq,
+                         const long long* krows, long long nk, int nthreads,
+                         double* dq, double* dk, double* dv) {
+  if (!q || !k || !v || !dout) return -1;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const long long BH = (long long)B * H;
+  if (!qrows) nq = BH * Nq;
+  if (!krows) nk = BH * Nk;
+  if ((nq > 0 && !dq) || (nk > 0 && (!dk || !dv))) return -1;
+  for (long long n = 0; qrows && n < nq; ++n)
+    if (qrows[n] < 0 || qrows[n] >= BH * Nq) return -1;
+  for (long long n = 0; krows && n < nk; ++n)
+    if (krows[n] < 0 || krows[n] >= BH * Nk) return -1;
+
+  int failed = 0;
+  /* dQ rows: each needs only its own row statistics */
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!s || !o) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (long long n = 0; n < nq; ++n) {
+      long long r = qrows ? qrows[n] : n;
+      long long bh = r / Nq;
+      double lse, dsum;
+      double* out = dq + (size_t)n * d;
+      for (int t = 0; t < d; ++t) out[t] = 0.0;
+      if (!s || !o) continue;
+      row_stats(q, k, v, dout, dtype, H, Nq, Nk, d, scale, causal, r, s, o, &lse, &dsum);
+      if (lse == -INFINITY) continue; /* empty row: P = 0 */
+      for (int j = 0; j < Nk; ++j) {
+        double sc = score(q, k, dtype, Nq, Nk, d, scale, causal, r, j);
+        if (sc == -INFINITY) continue;
+        double p = exp(sc - lse);
+        double ds = p * (dprob(dout, v, dtype, Nq, Nk, d, r, j) - dsum);
+        size_t koff = ((size_t)bh * Nk + j) * d;
+        for (int t = 0; t < d; ++t) out[t] += scale * ds * widen(k, dtype, koff + t);
+      }
+    }
+    free(s);
+    free(o);
+  }
+
+  if (failed) return -1;
+  if (nk == 0) return 0;
+  /* row statistics of every query row of the heads that requested key rows belong to */
+  char* need = (char*)calloc((size_t)BH, 1);
+  double* lse_all = (double*)malloc(sizeof(double) * (size_t)(BH * Nq));
+  double* dsum_all = (double*)malloc(sizeof(double) * (size_t)(BH * Nq));
+  if (!need || !lse_all || !dsum_all) {
+    free(need); free(lse_all); free(dsum_all);
+    return -1;
+  }
+  for (long long n = 0; n < nk; ++n) need[(krows ? krows[n] : n) / Nk] = 1;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!s || !o) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 16)
+    for (long long r = 0; r < BH * Nq; ++r) {
+      if (!need[r / Nq] || !s || !o) continue;
+      row_stats(q, k, v, dout, dtype, H, Nq, Nk, d, scale, causal, r, s, o,
+                lse_all + r, dsum_all + r);
+    }
+    free(s);
+    free(o);
+  }
+  if (failed) {
+    free(need); free(lse_all); free(dsum_all);
+    return -1;
+  }
+
+  /* dK and dV rows: sum over the query rows of the key's head */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (long long n = 0; n < nk; ++n) {
+    long long kr = krows ? krows[n] : n;
+    long long bh = kr / Nk;
+    int j = (int)(kr % Nk);
+    double* gk = dk + (size_t)n * d;
+    double* gv = dv + (size_t)n * d;
+    for (int t = 0; t < d; ++t) gk[t] = gv[t] = 0.0;
+    for (int i = 0; i < Nq; ++i) {
+      long long r = bh * Nq + i;
+      if (lse_all[r] == -INFINITY) continue;
+      double sc = score(q, k, dtype, Nq, Nk, d, scale, causal, r, j);
+      if (sc == -INFINITY) continue;
+      double p = exp(sc - lse_all[r]);
+      double ds = p * (dprob(dout, v, dtype, Nq, Nk, d, r, j) - dsum_all[r]);
+      size_t off = (size_t)r * d;
+      for (int t = 0; t < d; ++t) {
+        gv[t] += p * widen(dout, dtype, off + t);
+        gk[t] += scale * ds * widen(q, dtype, off + t);
+      }
+    }
+  }
+  free(need); free(lse_all); free(dsum_all);
   return 0;
 }
