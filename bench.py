@@ -122,6 +122,43 @@ def prefill_record(num: int, steps: int, warmup: int):
     return rec, (w, q, k, v)
 
 
+def bwd_record(num: int, steps: int, warmup: int):
+    """fa_bwd over workload `num` with the seeded dO; o and lse from fa_fwd (not timed)."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[num]
+    q, k, v = W.make_inputs(w, "cuda")
+    do = W.make_grad(w, "cuda")
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.B, w.H, w.Nk, w.d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = torch.empty((fa.bwd_workspace_bytes(w.B, w.H, w.Nq),), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+               workspace=ws)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    achieved = w.bwd_flops / (ev_ms * 1e-3) / 1e12
+    rec = {
+        "workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+        "causal": w.causal, "flops_per_call": w.bwd_flops,
+        "flops_note": "five contractions (S, dV, dP, dQ, dK), 10*B*H*Nq*Nk*d, halved if causal; "
+                      "the kernels execute seven (S and dP again in the dQ kernel)",
+        "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "note": "kernel_ms spans the three launches of one call (statistics, dK/dV, dQ)",
+        "tflops": w.bwd_flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+    }
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def decode_record(steps: int, warmup: int):
     import torch
     import exact_tiled_attention_08_amd as fa
@@ -170,7 +207,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
     args = ap.parse_args()
@@ -190,6 +227,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps({"copy": copy_record(args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps({"backward": bwd_record(args.workload, args.steps, args.warmup)}), flush=True)
         return
 
     main_rec, (w, q, k, v) = prefill_record(args.workload, args.steps, args.warmup)
@@ -224,6 +264,7 @@ def main():
         extra["prefill_N30000"] = rec4
         torch.cuda.empty_cache()
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
+        extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         out["also"] = extra
     print(json.dumps(out), flush=True)
 

@@ -7,6 +7,7 @@ not on the GPU, the call raises.
 
     o, lse = fwd(q, k, v, scale=None, causal=False)        # prefill
     o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, scale=None, causal=False)   # gradients
 
 Shapes are [B, H, N, d] (d innermost, contiguous); o is float32 [B, H, Nq, d],
 lse float32 [B, H, Nq]. The C header include/fa.h states the full contract.
@@ -17,8 +18,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode", "decode_workspace_bytes", "status_str", "library", "FaError",
-           "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
+           "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,14 +30,17 @@ FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_status_str",
-           "fa_last_hip_error", "fa_last_hip_error_str")
+EXPORTS = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_bwd_workspace_bytes",
+           "fa_bwd", "fa_status_str", "fa_last_hip_error", "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
+    "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
+                    _sz, _i, _vp]),
     "fa_status_str": (ctypes.c_char_p, [_i]),
     "fa_last_hip_error": (_i, []),
     "fa_last_hip_error_str": (ctypes.c_char_p, []),
@@ -84,6 +88,10 @@ def status_str(status: int) -> str:
 
 def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
     return int(library().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:
+    return int(library().fa_bwd_workspace_bytes(B, H, Nq))
 
 
 def _raise(status: int, what: str):
@@ -179,3 +187,45 @@ def decode(q, k, v, num_splits: int = 64, scale: float | None = None, out=None, 
         workspace.numel() * workspace.element_size(), _dtype_code(q), _stream_ptr(q.device))
     _raise(st, "fa_decode_splitkv")
     return out, lse
+
+
+def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, dq=None, dk=None,
+        dv=None, workspace=None):
+    """Attention backward on the GPU: gradients (dq, dk, dv), float32, of a loss with respect
+    to q, k, v given do = dL/dO and the (o, lse) that fwd returned for the same inputs."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if not isinstance(do, torch.Tensor) or do.shape != q.shape or do.dtype != q.dtype \
+            or not do.is_contiguous() or do.device != q.device:
+        raise ValueError("do must be a contiguous tensor of q's shape, dtype and device")
+    if not isinstance(o, torch.Tensor) or o.shape != (B, H, Nq, d) or o.dtype != torch.float32 \
+            or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be the contiguous float32 [B, H, Nq, d] output of fwd")
+    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, Nq) or lse.dtype != torch.float32 \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be the contiguous float32 [B, H, Nq] output of fwd")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def out(t, shape):
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=q.device)
+        if t.shape != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"gradient outputs must be contiguous float32 {shape} tensors")
+        return t
+
+    dq = out(dq, (B, H, Nq, d))
+    dk = out(dk, (B, H, Nk, d))
+    dv = out(dv, (B, H, Nk, d))
+    need = bwd_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    st = library().fa_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d, float(scale),
+        int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _dtype_code(q), _stream_ptr(q.device))
+    _raise(st, "fa_bwd")
+    return dq, dk, dv

@@ -42,7 +42,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "a size is < 1 or the sizes overflow the index range";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or size";
-    case FA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+    case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     case FA_ERR_VALUE: return "scale must be finite and > 0; causal must be 0 or 1";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
@@ -132,6 +132,63 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   hipError_t e = fa::launch_decode(p, d, dtype == FA_BF16, (hipStream_t)stream);
   return finish_launch(e);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
+  if (B < 1 || H < 1 || Nq < 1) return 0;
+  const unsigned long long pad = ((unsigned long long)Nq + fa::kBwdQueryRows - 1) / fa::kBwdQueryRows *
+                                 fa::kBwdQueryRows;
+  const unsigned long long n = (unsigned long long)B * H * pad;
+  if (n > (1ull << 60) / 8ull) return 0;
+  return (size_t)(n * 8ull);  // two float32 statistics per (padded) query row
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                 const void* dout, float* dq, float* dk, float* dv, int B, int H, int Nq, int Nk,
+                 int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                 fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_VALUE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      ((uintptr_t)lse & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const long long nkt = (Nk + fa::kBwdKeyRows - 1) / fa::kBwdKeyRows;
+  const long long nqt = (Nq + fa::kBwdQueryRows - 1) / fa::kBwdQueryRows;
+  if (BH * nkt > INT32_MAX || BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws = (float*)workspace;
+  p.BH = (int)BH;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.Nq_pad = (int)(nqt * fa::kBwdQueryRows);
+  p.off = Nk - Nq;
+  p.nkt = (int)nkt;
+  p.nqt = (int)nqt;
+  p.hpg_kv = heads_per_group((int)BH, nkt);
+  p.hpg_q = heads_per_group((int)BH, nqt);
+  p.scale = scale;
+  p.c = scale * fa::kLog2e;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  return finish_launch(fa::launch_bwd(p, d, causal != 0, (hipStream_t)stream));
 }
 
 }  // extern "C"

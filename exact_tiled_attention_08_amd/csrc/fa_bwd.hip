@@ -1,0 +1,437 @@
+// Attention backward for bfloat16 Q/K/V/dO on gfx950: bf16 MFMA, float32 accumulation.
+//
+// Gradients of a loss L with respect to Q, K and V given dO = dL/dO, for the attention of
+// fa_fwd. The probabilities are recomputed tile by tile from the saved per-row log-sum-exp
+// instead of being stored ("Flash Attention Optimization", section "Sizing a tile, and why
+// the backward pass recomputes instead of storing"; "Explain FlashAttention ...", section
+// "Exact attention, finite precision and backward"). With P_ij = exp(scale q_i.k_j - LSE_i)
+// (0 where masked), the chain rule through O = P V and the row softmax gives
+//
+//   dV_j = sum_i P_ij dO_i          dP_ij = dO_i . v_j          D_i = dO_i . O_i
+//   dS_ij = P_ij (dP_ij - D_i)      dQ_i = scale sum_j dS_ij k_j    dK_j = scale sum_i dS_ij q_i
+//
+// (D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.)
+//
+// Three launches on one stream:
+//   1. bwd_pre_kernel: D_i and LSE_i in log2 units per query row, into the workspace.
+//   2. bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h); each of its 4 waves keeps
+//      32 keys' K and V rows in VGPRs and their dK, dV in float32 accumulators while the
+//      query tiles (Q, dO and the row statistics, 64 rows each) stream through LDS.
+//   3. bwd_dq_kernel: one workgroup per 128 query rows of one (b, h); each wave keeps 32
+//      rows' Q and dO in VGPRs and its dQ in float32 accumulators while 64-key K and V tiles
+//      stream through LDS. It recomputes S and dP rather than adding partial dQ from the
+//      dK/dV workgroups with atomics: every output element is written once, in a fixed
+//      order, so the result is deterministic.
+//
+// MFMA layouts (v_mfma_f32_32x32x16_bf16, lane l, g = l / 32):
+//   A (32 x 16): row l%32, k = 8g..8g+7      B (16 x 32): col l%32, same k
+//   C (32 x 32): col l%32, row 8*(i/4) + 4g + i%4 for element i = 0..15
+// dK/dV kernel: S = Q K^T and dP = dO V^T put one KEY per lane column (16 queries per
+// lane), so S, P, dP and dS convert in place into the B operands of dV^T = dO^T P and
+// dK^T = Q^T dS; the A operands dO^T and Q^T come from row-major LDS tiles through the
+// transpose read ds_read_b64_tr_b16, in the query order of the B operand (lane half g holds
+// queries {4g..4g+3, 8+4g..8+4g+3} of each 16-query step). The dQ kernel is the mirror
+// image: S^T = K Q^T and dP^T = V dO^T put one QUERY per lane column and dQ^T = K^T dS^T
+// reads K^T by transpose.
+//
+// Precision: P and dS are rounded to bfloat16 (nearest even) as MFMA operands; S, dP, the
+// statistics and every accumulation are float32; outputs are float32.
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kT = 256;    // threads per workgroup of the two main kernels (4 waves)
+constexpr int kRows = 64;  // rows per LDS tile: queries (dK/dV kernel), keys (dQ kernel)
+
+template <int D>
+struct BCfg {
+  static constexpr int ROWB = 2 * D;                // bytes per bf16 row
+  static constexpr int CHR = D / 8;                 // 16-byte chunks per row
+  static constexpr int TILEB = kRows * ROWB;        // bytes of one tile
+  static constexpr int LOADS = kRows * CHR / kT;    // direct loads per thread per tile
+  static constexpr int ROWSTEP = kT / CHR;          // rows between a thread's slots
+  static_assert(kRows * CHR % kT == 0 && ROWSTEP % 16 == 0, "tile split");
+};
+
+// XOR swizzle of the 16-byte chunks of LDS row r: chunk c sits at chunk position
+// c ^ bswz(r). Every tile is read in two patterns and both must be free of bank conflicts
+// on the 64 banks of 4 bytes:
+//  (a) ds_read_b128 of one chunk from 16 consecutive rows (16 lanes per LDS cycle):
+//      bswz must be a bijection on the row bits that select the bank;
+//  (b) ds_read_b64_tr_b16 of 4 consecutive chunks from 4 consecutive rows (32 lanes):
+//      the chunk-group bits of bswz (bit 2 and up) must differ between those rows.
+// d = 128 (256-byte rows span all banks): bswz = rotation of r's low four bits.
+// d = 64 (128-byte rows, odd rows in the upper half of the banks): rotation of bits 1..3.
+template <int CHR>
+__device__ __forceinline__ int bswz(int r) {
+  return CHR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Pattern (a): 8 bf16 of chunk c of row r (an A operand row fragment).
+template <int D>
+__device__ __forceinline__ bf16x8 rfrag(const char* t, int r, int c) {
+  return *(const bf16x8*)(t + r * (2 * D) + 16 * (c ^ bswz<D / 8>(r)));
+}
+
+// Pattern (b): the A operand (32 columns x 16 rows of the tile, transposed) for the 16-row
+// step starting at row r0 and the 32-column block db: lane l gets column 32*db + l%32 at
+// rows r0 + {4g..4g+3, 8+4g..8+4g+3}.
+template <int D>
+__device__ __forceinline__ bf16x8 tfrag(const char* t, int r0, int db, int lane) {
+  const int g = lane >> 5, trG = (lane >> 4) & 1, trj = lane & 15;
+  bf16x4 half[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + 8 * h + 4 * g + (trj >> 2);
+    const int cbyte = 64 * db + 32 * trG + 8 * (trj & 3);
+    const int addr = r * (2 * D) + 16 * ((cbyte >> 4) ^ bswz<D / 8>(r)) + (cbyte & 15);
+    half[h] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + addr)));
+  }
+  return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)((const lds_char*)p);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Offset of the statistics of query row i inside one head's workspace block.
+__device__ __forceinline__ int stat_index(int i) { return (i >> 6) * 128 + (i & 63); }
+
+// ---------------------------------------------------------------- row statistics
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;         // threads per row, 8 elements each
+  constexpr int RPB = 256 / TPR;     // rows per block
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / TPR;  // over BH * Nq_pad
+  const int part = tid % TPR;
+  const long long total = (long long)p.BH * p.Nq_pad;
+  const int bh = (int)(row / p.Nq_pad);
+  const int i = (int)(row - (long long)bh * p.Nq_pad);
+  float acc = 0.f;
+  float l2 = INFINITY;
+  if (row < total && i < p.Nq) {
+    const size_t e = ((size_t)bh * p.Nq + i) * D + 8 * part;
+    const bf16x8 dov = *(const bf16x8*)((const __bf16*)p.dout + e);
+    const f32x4 o0 = *(const f32x4*)(p.o + e);
+    const f32x4 o1 = *(const f32x4*)(p.o + e + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc = __builtin_fmaf((float)dov[t], o0[t], acc);
+      acc = __builtin_fmaf((float)dov[4 + t], o1[t], acc);
+    }
+    const float L = p.lse[(size_t)bh * p.Nq + i];
+    l2 = (L == -INFINITY) ? INFINITY : L * kLog2e;
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+  if (row < total && part == 0) {
+    float* w = p.ws + (size_t)bh * p.Nq_pad * 2 + stat_index(i);
+    w[0] = l2;
+    w[64] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int STAGE = 2 * C::TILEB + 512;  // Q tile, dO tile, 64 LSE2 + 64 D values
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int col = lane & 31;
+
+  // Low key tiles see the most queries under the causal mask; ascending order issues them first.
+  int bh, kt;
+  map_block(blockIdx.x, gridDim.x, p.nkt, p.hpg_kv, false, bh, kt);
+  const int k0 = kt * kBwdKeyRows;
+  const int kw0 = k0 + 32 * w;  // first key of this wave
+  const int key = kw0 + col;    // this lane's key
+
+  const __bf16* __restrict__ qh = (const __bf16*)p.q + (size_t)bh * p.Nq * D;
+  const __bf16* __restrict__ doh = (const __bf16*)p.dout + (size_t)bh * p.Nq * D;
+  const __bf16* __restrict__ kh = (const __bf16*)p.k + (size_t)bh * p.Nk * D;
+  const __bf16* __restrict__ vh = (const __bf16*)p.v + (size_t)bh * p.Nk * D;
+  const float* __restrict__ wsh = p.ws + (size_t)bh * p.Nq_pad * 2;
+
+  // K and V rows of this lane's key: the B operands of S = Q K^T and dP = dO V^T. Keys past
+  // Nk are zero; their columns are independent of every other column and are not stored.
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (key < p.Nk) {
+      kf[kk] = *(const bf16x8*)(kh + (size_t)key * D + 16 * kk + 8 * g);
+      vf[kk] = *(const bf16x8*)(vh + (size_t)key * D + 16 * kk + 8 * g);
+    } else {
+      kf[kk] = bf16x8{};
+      vf[kk] = bf16x8{};
+    }
+  }
+
+  // Query tiles to visit: under the causal mask query i sees key j iff j <= i + off, so
+  // the first query that sees key k0 is k0 - off.
+  const int q_begin = CAUSAL ? max(0, k0 - p.off) : 0;
+  const int t0 = q_begin / kRows;
+  const int t1 = (p.Nq + kRows - 1) / kRows;
+
+  // Direct loads: slot s = n*kT + tid holds chunk position s % CHR of tile row s / CHR; the
+  // swizzle depends only on row bits that repeat every ROWSTEP rows.
+  const int lrow = tid / C::CHR;
+  const uint32_t lchunk = 16u * (uint32_t)((tid % C::CHR) ^ bswz<C::CHR>(lrow));
+  auto stage = [&](int i) -> char* { return smem + i * STAGE; };
+  auto issue = [&](int t, char* st) {
+    const int r0 = t * kRows;
+#pragma unroll
+    for (int n = 0; n < C::LOADS; ++n) {
+      const int row = min(lrow + n * C::ROWSTEP, p.Nq - 1 - r0);  // rows past Nq repeat row Nq-1
+      const uint32_t off = (uint32_t)(row * C::ROWB) + lchunk;
+      const uint32_t dst = (uint32_t)((n * kT + 64 * w) * 16);
+      dma16(qh + (size_t)r0 * D, off, lds_addr(st + dst));
+      dma16(doh + (size_t)r0 * D, off, lds_addr(st + C::TILEB + dst));
+    }
+    // 512 bytes of statistics: lanes 0..15 the LSE2 values, 16..31 the D values
+    if (w == 0 && lane < 32) dma16(wsh + (size_t)t * 128, 16u * lane, lds_addr(st + 2 * C::TILEB));
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  if (t0 < t1) issue(t0, stage(0));
+  for (int t = t0; t < t1; ++t) {
+    const int cur = (t - t0) & 1;
+    wait_loads();  // tile t (the only loads in flight)
+    wg_barrier();  // tile t visible to all; everyone is done with the other stage
+    if (t + 1 < t1) issue(t + 1, stage(cur ^ 1));
+    const char* Qs = stage(cur);
+    const char* dOs = Qs + C::TILEB;
+    const float* sts = (const float*)(Qs + 2 * C::TILEB);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qa = t * kRows + 32 * qs;  // first query of this 32-row step
+      if (qa >= p.Nq) continue;           // padding rows only
+      if (CAUSAL && qa + 31 + p.off < kw0) continue;  // no query here sees a key of this wave
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma(rfrag<D>(Qs, 32 * qs + col, 2 * kk + g), kf[kk], s);
+        dp = mfma(rfrag<D>(dOs, 32 * qs + col, 2 * kk + g), vf[kk], dp);
+      }
+      // element i of this lane: query qa + 8(i/4) + 4g + i%4, key `key`
+      const bool need_mask = CAUSAL && (qa + p.off < kw0 + 31);
+      const int lim = key - p.off - qa - 4 * g;  // visible iff 8(i/4) + i%4 >= lim
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *(const f32x4*)(sts + 32 * qs + 8 * j + 4 * g);
+        const f32x4 d4 = *(const f32x4*)(sts + 64 + 32 * qs + 8 * j + 4 * g);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * j + u;
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -l4[u]));
+          if (need_mask && 8 * j + u < lim) pe = 0.f;
+          const float ds = pe * (dp[i] - d4[u]);
+          pb[i >> 3][i & 7] = (__bf16)pe;
+          dsb[i >> 3][i & 7] = (__bf16)ds;
+        }
+      }
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dv[db] = mfma(tfrag<D>(dOs, 32 * qs + 16 * st2, db, lane), pb[st2], dv[db]);
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dk[db] = mfma(tfrag<D>(Qs, 32 * qs + 16 * st2, db, lane), dsb[st2], dk[db]);
+    }
+  }
+
+  // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4.
+  if (key < p.Nk) {
+    float* dkr = p.dk + ((size_t)bh * p.Nk + key) * D;
+    float* dvr = p.dv + ((size_t)bh * p.Nk + key) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 a, b;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = dk[db][4 * j + u] * p.scale;
+          b[u] = dv[db][4 * j + u];
+        }
+        *(f32x4*)(dkr + 32 * db + 8 * j + 4 * g) = a;
+        *(f32x4*)(dvr + 32 * db + 8 * j + 4 * g) = b;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int STAGE = 2 * C::TILEB;  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int col = lane & 31;
+
+  int bh, qt;
+  map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg_q, CAUSAL, bh, qt);
+  const int q0 = qt * kBwdQueryRows;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + col;
+
+  const __bf16* __restrict__ qh = (const __bf16*)p.q + (size_t)bh * p.Nq * D;
+  const __bf16* __restrict__ doh = (const __bf16*)p.dout + (size_t)bh * p.Nq * D;
+  const __bf16* __restrict__ kh = (const __bf16*)p.k + (size_t)bh * p.Nk * D;
+  const __bf16* __restrict__ vh = (const __bf16*)p.v + (size_t)bh * p.Nk * D;
+  const float* __restrict__ wsh = p.ws + (size_t)bh * p.Nq_pad * 2;
+
+  // Q and dO rows of this lane's query: B operands of S^T = K Q^T and dP^T = V dO^T.
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (qrow < p.Nq) {
+      qf[kk] = *(const bf16x8*)(qh + (size_t)qrow * D + 16 * kk + 8 * g);
+      df[kk] = *(const bf16x8*)(doh + (size_t)qrow * D + 16 * kk + 8 * g);
+    } else {
+      qf[kk] = bf16x8{};
+      df[kk] = bf16x8{};
+    }
+  }
+  // padding rows (qrow >= Nq, < Nq_pad) carry LSE2 = +inf: their probabilities are 0
+  const float lse2 = wsh[stat_index(qrow)];
+  const float dsum = wsh[stat_index(qrow) + 64];
+
+  int kv_end = p.Nk;
+  int wave_kv_end = (wq0 < p.Nq) ? p.Nk : 0;
+  if (CAUSAL) {
+    const int last_q = min(q0 + kBwdQueryRows, p.Nq) - 1;
+    kv_end = min(p.Nk, last_q + p.off + 1);
+    if (wq0 < p.Nq) wave_kv_end = min(p.Nk, min(wq0 + 31, p.Nq - 1) + p.off + 1);
+  }
+  const int ntiles = kv_end > 0 ? (kv_end + kRows - 1) / kRows : 0;
+
+  const int lrow = tid / C::CHR;
+  const uint32_t lchunk = 16u * (uint32_t)((tid % C::CHR) ^ bswz<C::CHR>(lrow));
+  auto stage = [&](int i) -> char* { return smem + i * STAGE; };
+  auto issue = [&](int t, char* st) {
+    const int r0 = t * kRows;
+#pragma unroll
+    for (int n = 0; n < C::LOADS; ++n) {
+      const int row = min(lrow + n * C::ROWSTEP, p.Nk - 1 - r0);  // rows past Nk repeat row Nk-1
+      const uint32_t off = (uint32_t)(row * C::ROWB) + lchunk;
+      const uint32_t dst = (uint32_t)((n * kT + 64 * w) * 16);
+      dma16(kh + (size_t)r0 * D, off, lds_addr(st + dst));
+      dma16(vh + (size_t)r0 * D, off, lds_addr(st + C::TILEB + dst));
+    }
+  };
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+  if (ntiles > 0) issue(0, stage(0));
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    wait_loads();
+    wg_barrier();
+    if (t + 1 < ntiles) issue(t + 1, stage(cur ^ 1));
+    const char* Ks = stage(cur);
+    const char* Vs = Ks + C::TILEB;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int ka = t * kRows + 32 * kb;  // first key of this 32-key block
+      if (ka >= wave_kv_end) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma(rfrag<D>(Ks, 32 * kb + col, 2 * kk + g), qf[kk], s);
+        dp = mfma(rfrag<D>(Vs, 32 * kb + col, 2 * kk + g), df[kk], dp);
+      }
+      // element i: key ka + 8(i/4) + 4g + i%4, query qrow
+      const bool need_mask = (ka + 32 > p.Nk) || (CAUSAL && ka + 31 > wq0 + p.off);
+      const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - ka - 4 * g;
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
+        if (need_mask && 8 * (i >> 2) + (i & 3) > lim) pe = 0.f;
+        dsb[i >> 3][i & 7] = (__bf16)(pe * (dp[i] - dsum));
+      }
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dq[db] = mfma(tfrag<D>(Ks, 32 * kb + 16 * st2, db, lane), dsb[st2], dq[db]);
+    }
+  }
+
+  // dQ^T: lane column = query, element i = dim 32db + 8(i/4) + 4g + i%4.
+  if (qrow < p.Nq) {
+    float* dqr = p.dq + ((size_t)bh * p.Nq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 a;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = dq[db][4 * j + u] * p.scale;
+        *(f32x4*)(dqr + 32 * db + 8 * j + 4 * g) = a;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch(const BwdParams& prm, bool causal, hipStream_t s) {
+  BwdParams p = prm;
+  constexpr int RPB = 256 / (D / 8);
+  const long long rows = (long long)p.BH * p.Nq_pad;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned nkv = (unsigned)(p.BH * p.nkt), nq = (unsigned)(p.BH * p.nqt);
+  if (causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(nkv), dim3(kT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(nq), dim3(kT), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(nkv), dim3(kT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(nq), dim3(kT), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return launch<128>(p, causal, s);
+  return launch<64>(p, causal, s);
+}
+
+}  // namespace fa

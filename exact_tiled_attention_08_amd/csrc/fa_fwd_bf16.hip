@@ -86,34 +86,6 @@ __device__ __forceinline__ int swz_v(int r, int c) {
   return CHR == 16 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
 }
 
-// Workgroup barrier without the memory fence of __syncthreads(): the fence would also wait
-// for this wave's in-flight direct-to-LDS loads, which must keep flying across the phase
-// barrier. LDS reads are drained first; loads are waited for explicitly where their data
-// is needed. The "memory" clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// One global_load_lds_dwordx4: each lane copies 16 bytes from (uniform base + its 32-bit
-// byte offset) to LDS byte address lds_base + 16*lane (lds_base wave-uniform, in M0).
-// Written as inline asm so that the compiler does not treat later LDS reads of OTHER
-// buffers as possible readers of this copy and stall them on vmcnt; completion is awaited
-// explicitly with wait_loads() before the barrier that publishes the buffer. The offset
-// register is the caller's long-lived VGPR, so no later instruction overwrites it while
-// the load is in flight. M0 is saved and restored around the copy.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
 __device__ __forceinline__ float wave_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

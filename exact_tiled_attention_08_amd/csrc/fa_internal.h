@@ -46,14 +46,75 @@ struct DecodeParams {
   float c;        // scale * log2(e)
 };
 
+// Arguments of the backward kernels.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* o;     // forward output [BH][Nq][d]
+  const float* lse;   // forward log-sum-exp [BH][Nq] (natural log)
+  const void* dout;   // gradient of the loss with respect to O, [BH][Nq][d]
+  float* dq;
+  float* dk;
+  float* dv;
+  // Row statistics [BH][Nq_pad / 64][2][64]: per block of 64 query rows, the 64 LSEs in
+  // log2 units (+inf for rows that see no key and for padding rows, so that their
+  // probabilities come out 0), then the 64 values sum_t dO[i][t] * O[i][t] (0 for padding).
+  float* ws;
+  int BH;
+  int Nq;
+  int Nk;
+  int Nq_pad;         // Nq rounded up to a whole number of dQ query tiles
+  int off;            // Nk - Nq
+  int nkt;            // key tiles per (b, h) of the dK/dV kernel
+  int nqt;            // query tiles per (b, h) of the dQ kernel
+  int hpg_kv;         // (b, h) pairs per XCD group, dK/dV kernel
+  int hpg_q;          // (b, h) pairs per XCD group, dQ kernel
+  float scale;
+  float c;            // scale * log2(e)
+};
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence would also wait
+// for this wave's in-flight direct-to-LDS loads, which must keep flying across the phase
+// barrier. LDS reads are drained first; loads are waited for explicitly where their data
+// is needed. The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One global_load_lds_dwordx4: each lane copies 16 bytes from (uniform base + its 32-bit
+// byte offset) to LDS byte address lds_base + 16*lane (lds_base wave-uniform, in M0).
+// Written as inline asm so that the compiler does not treat later LDS reads of OTHER
+// buffers as possible readers of this copy and stall them on vmcnt; completion is awaited
+// explicitly with wait_loads() before the barrier that publishes the buffer. The offset
+// register is the caller's long-lived VGPR, so no later instruction overwrites it while
+// the load is in flight. M0 is saved and restored around the copy.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
 // Launchers (defined next to their kernels). Each returns the hipError_t of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 // Query rows per workgroup of each prefill kernel (host needs it for the grid).
 int fwd_bf16_block_rows(int d);
 int fwd_f32_block_rows(int d);
+
+// Key rows per dK/dV workgroup and query rows per dQ workgroup of the backward pass.
+constexpr int kBwdKeyRows = 128;
+constexpr int kBwdQueryRows = 128;
 
 // Block -> (b*H + h, query tile) mapping shared by the prefill kernels.
 //

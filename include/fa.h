@@ -56,7 +56,7 @@ typedef enum {
   FA_ERR_NULL = -1,         /* a required pointer is NULL                          */
   FA_ERR_SHAPE = -2,        /* a size is < 1, or sizes overflow the index range    */
   FA_ERR_UNSUPPORTED = -3,  /* valid but not implemented: head dim, dtype, size    */
-  FA_ERR_WORKSPACE = -4,    /* decode workspace NULL or smaller than required      */
+  FA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than required             */
   FA_ERR_HIP = -5,          /* the HIP runtime reported an error at launch         */
   FA_ERR_VALUE = -6,        /* scale not finite and > 0, causal not 0/1, ...       */
   FA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned             */
@@ -103,6 +103,39 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
                             int B, int H, int Nk, int d, float scale, int num_splits,
                             void* workspace, size_t workspace_bytes, fa_dtype dtype,
                             void* stream);
+
+/*
+ * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs:
+ * B*H*ceil(Nq/128)*128*8 (two float32 statistics per query row, rows padded to a whole
+ * number of 128-row tiles). Returns 0 if an argument is < 1 or the size overflows.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
+
+/*
+ * fa_bwd — attention backward: the gradients of a loss L with respect to q, k and v, given
+ * do = dL/dO and the o and lse that fa_fwd returned for the same q, k, v, scale and causal.
+ * The probabilities are recomputed tile by tile from lse rather than stored ("Flash
+ * Attention Optimization", section "Sizing a tile, and why the backward pass recomputes
+ * instead of storing"; "Explain FlashAttention ...", section "Exact attention, finite
+ * precision and backward"); with P = softmax(S) as in fa_fwd, the chain rule gives
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q        (masked pairs contribute nothing).
+ *   q, do [B][H][Nq][d]  dtype         k, v [B][H][Nk][d]  dtype
+ *   o     [B][H][Nq][d]  float32       lse  [B][H][Nq] float32 (as written by fa_fwd;
+ *                                      a row with LSE = -inf contributes nothing)
+ *   dq    [B][H][Nq][d]  float32, dk, dv [B][H][Nk][d] float32 (written; every element)
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(B, H, Nq) bytes, 16-byte
+ *   aligned, owned by the caller; contents on entry are ignored, on return unspecified.
+ *   dtype: FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). d in {64, 128}; B, H, Nq, Nk >= 1;
+ *   Nq * d, Nk * d <= 2^30. scale finite and > 0; causal 0 or 1 (the same alignment as
+ *   fa_fwd). lse only needs 4-byte alignment. Three kernels run in order on `stream`;
+ *   every output element is written exactly once (deterministic, no atomics). P and dS are
+ *   rounded to bfloat16 as MFMA operands; everything else is float32.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                 const void* dout, float* dq, float* dk, float* dv, int B, int H, int Nq, int Nk,
+                 int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                 fa_dtype dtype, void* stream);
 
 /* fa_status_str — static English description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

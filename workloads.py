@@ -9,7 +9,8 @@ target device is seeded with ``10*c + t`` (c = workload number 1..5, t = 0 for
 Q, 1 for K, 2 for V); then, for b = 0..B-1 in order, one ``torch.randn`` call
 draws the [H, N, d] float32 slice, which is multiplied by the workload's scale
 factor and rounded to the storage dtype (bfloat16 rounding is
-round-to-nearest-even). The oracle always consumes the rounded bytes, so input
+round-to-nearest-even). The backward pass takes a fourth tensor, dO, drawn the same way
+with t = 3 and factor 1. The oracle always consumes the rounded bytes, so input
 quantisation is never counted as kernel error. Different devices give
 different (equally valid) draws for one seed; a test always reads back the
 bytes the kernel received.
@@ -45,6 +46,13 @@ class Workload:
     def flops(self) -> float:
         """Algorithmic FLOPs of the two contractions: 4*B*H*Nq*Nk*d, halved if causal."""
         f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def bwd_flops(self) -> float:
+        """Algorithmic FLOPs of the backward pass: the five contractions S = QK^T, dV = P^T dO,
+        dP = dO V^T, dQ = dS K and dK = dS^T Q, 2*Nq*Nk*d each per head, halved if causal."""
+        f = 10.0 * self.B * self.H * self.Nq * self.Nk * self.d
         return f / 2 if self.causal else f
 
     @property
@@ -95,6 +103,11 @@ def make_inputs(w: Workload, device="cpu"):
     k = draw((w.B, w.H, w.Nk, w.d), 10 * c + 1, w.qk_mult, w.dtype, device)
     v = draw((w.B, w.H, w.Nk, w.d), 10 * c + 2, 1.0, w.dtype, device)
     return q, k, v
+
+
+def make_grad(w: Workload, device="cpu"):
+    """dO, the gradient fed to the backward pass: N(0,1) of q's shape and dtype, seed 10c + 3."""
+    return draw((w.B, w.H, w.Nq, w.d), 10 * w.number + 3, 1.0, w.dtype, device)
 
 
 def sample_rows(w: Workload, per_head: int = 64, seed: int = 12345):
