@@ -8,7 +8,10 @@ only the seeded input generators in ``workloads.py``.
 ``attention`` evaluates the plain definition O = softmax(Q K^T * scale + mask) V
 row by row in double precision (the C source states each passage it follows);
 ``attention_bwd`` evaluates the gradients of sum(O * dO) with respect to Q, K, V
-from the same definition by the chain rule.
+from the same definition by the chain rule. ``paged_attention`` is the same definition
+for one query per sequence whose keys and values live in a paged cache: it first
+gathers each sequence's logical key/value rows through its block table, then calls
+``attention``.
 """
 from __future__ import annotations
 
@@ -182,3 +185,51 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, qrows=None, k
     if rc != 0:
         raise ValueError("oracle_attention_bwd rejected its arguments")
     return dq, dk, dv
+
+
+def paged_gather(cache, block_table, seq_len: int, b: int, page_size: int):
+    """Logical rows of sequence b from a paged cache, as [H, seq_len, d].
+
+    cache [num_pages, page_size, H, d]; block_table [B, max_pages] (int). The key at
+    logical position t of sequence b is cache[block_table[b, t // page_size], t % page_size]
+    (the page indirection of a paged key/value cache; "FlashAttention: Attention Is Limited
+    by Memory, Not Math", section "Where it helps, and where it does not", names engines
+    that pair split-KV decoding with paged caches). A page id outside [0, num_pages) holds
+    no keys: its positions are left out.
+    """
+    import torch
+    num_pages = cache.shape[0]
+    rows = []
+    for t in range(seq_len):
+        page = int(block_table[b, t // page_size])
+        if 0 <= page < num_pages:
+            rows.append(cache[page, t % page_size])      # [H, d]
+    if not rows:
+        return cache.new_zeros((cache.shape[2], 0, cache.shape[3]))
+    return torch.stack(rows, dim=1).contiguous()          # [H, n, d]
+
+
+def paged_attention(q, k_cache, v_cache, block_table, seq_lens, page_size: int, scale: float,
+                    threads: int | None = None):
+    """Float64 attention of one query per (b, h) over a paged cache.
+
+    q [B, H, 1, d]; k_cache, v_cache [num_pages, page_size, H, d] (float32 or bfloat16,
+    CPU tensors); block_table [B, max_pages] and seq_lens [B] (integers). Sequence b
+    attends to its first seq_lens[b] logical positions (all visible: one query at the end
+    of its sequence). Returns (o [B*H, d], lse [B*H]) float64; a sequence with no key
+    gets O = 0 and LSE = -inf.
+    """
+    B, H, nq, d = q.shape
+    if nq != 1:
+        raise ValueError("paged_attention takes one query per (b, h)")
+    o = np.zeros((B * H, d), np.float64)
+    lse = np.full((B * H,), -np.inf, np.float64)
+    for b in range(B):
+        kb = paged_gather(k_cache, block_table, int(seq_lens[b]), b, page_size)
+        vb = paged_gather(v_cache, block_table, int(seq_lens[b]), b, page_size)
+        if kb.shape[1] == 0:
+            continue
+        ob, lb = attention(q[b:b + 1], kb[None], vb[None], scale, False, threads=threads)
+        o[b * H:(b + 1) * H] = ob
+        lse[b * H:(b + 1) * H] = lb
+    return o, lse
