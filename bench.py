@@ -187,6 +187,45 @@ def decode_record(steps: int, warmup: int):
     return rec
 
 
+def paged_decode_record(steps: int, warmup: int, page_size: int = 64):
+    """fa_decode_paged on the decode workload's cache laid out in pages placed in a seeded
+    random order across the pool (same keys, same bytes, page-table addressing)."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[5]
+    q, k, v = W.make_inputs(w, "cuda")
+    kc, table = W.to_paged(k, page_size, 55)
+    del k
+    vc, _ = W.to_paged(v, page_size, 55)
+    del v
+    torch.cuda.empty_cache()
+    lens = torch.full((w.B,), w.Nk, dtype=torch.int32, device="cuda")
+    ws = torch.empty((fa.decode_workspace_bytes(w.B, w.H, w.d, w.num_splits),), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((w.B, w.H, 1, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.decode_paged(q, kc, vc, table, lens, num_splits=w.num_splits, scale=w.scale, out=o,
+                        lse=lse, workspace=ws)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    nbytes = w.io_bytes + table.numel() * 4 + lens.numel() * 4
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    rec = {
+        "workload": f"{w.name}, paged: {page_size}-key pages in shuffled pool order",
+        "B": w.B, "H": w.H, "Nk": w.Nk, "d": w.d, "num_splits": w.num_splits,
+        "page_size": page_size, "bytes_per_call": nbytes, "ms_per_step": wall_ms,
+        "kernel_ms": ev_ms, "note": "kernel_ms spans both launches of one call (split + merge)",
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+    }
+    del q, kc, vc
+    torch.cuda.empty_cache()
+    return rec
+
+
 def copy_record(steps: int, warmup: int):
     """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30 bytes each."""
     import torch
@@ -207,7 +246,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged"], default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
     args = ap.parse_args()
@@ -227,6 +266,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps({"copy": copy_record(args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "paged":
+        print(json.dumps({"decode_paged": paged_decode_record(args.steps, args.warmup)}), flush=True)
         return
     if args.only == "backward":
         print(json.dumps({"backward": bwd_record(args.workload, args.steps, args.warmup)}), flush=True)
@@ -264,6 +306,7 @@ def main():
         extra["prefill_N30000"] = rec4
         torch.cuda.empty_cache()
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
+        extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))
         extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         out["also"] = extra
     print(json.dumps(out), flush=True)

@@ -7,6 +7,7 @@ not on the GPU, the call raises.
 
     o, lse = fwd(q, k, v, scale=None, causal=False)        # prefill
     o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
+    o, lse = decode_paged(q, k_cache, v_cache, block_table, seq_lens)  # paged cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, scale=None, causal=False)   # gradients
 
 Shapes are [B, H, N, d] (d innermost, contiguous); o is float32 [B, H, Nq, d],
@@ -18,7 +19,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
+__all__ = ["fwd", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
            "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
@@ -30,14 +31,17 @@ FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_bwd_workspace_bytes",
-           "fa_bwd", "fa_status_str", "fa_last_hip_error", "fa_last_hip_error_str")
+EXPORTS = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_hip_error",
+           "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
+    "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
+                             _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _sz, _i, _vp]),
@@ -186,6 +190,47 @@ def decode(q, k, v, num_splits: int = 64, scale: float | None = None, out=None, 
         B, H, Nk, d, float(scale), int(num_splits), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _dtype_code(q), _stream_ptr(q.device))
     _raise(st, "fa_decode_splitkv")
+    return out, lse
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits: int = 64,
+                 scale: float | None = None, out=None, lse=None, workspace=None):
+    """Split-KV decode over a paged cache: q [B, H, 1, d]; k_cache, v_cache
+    [num_pages, page_size, H, d]; block_table int32 [B, max_pages]; seq_lens int32 [B] (all
+    on the GPU). Returns (o, lse)."""
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [B, H, 1, d]")
+    B, H, _, d = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[2] != H or k_cache.shape[3] != d \
+            or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, H, d] with q's H and d")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache and v_cache must share one dtype")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, 1, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    st = library().fa_decode_paged(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, d, page_size, num_pages,
+        block_table.shape[1], float(scale), int(num_splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _dtype_code(q), _stream_ptr(q.device))
+    _raise(st, "fa_decode_paged")
     return out, lse
 
 

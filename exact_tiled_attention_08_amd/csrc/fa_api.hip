@@ -115,7 +115,7 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
     return FA_ERR_ALIGN;
 
-  fa::DecodeParams p;
+  fa::DecodeParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -132,6 +132,53 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   hipError_t e = fa::launch_decode(p, d, dtype == FA_BF16, (hipStream_t)stream);
   return finish_launch(e);
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int* block_table, const int* seq_lens, float* o, float* lse,
+                          int B, int H, int d, int page_size, int num_pages, int max_pages_per_seq,
+                          float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          fa_dtype dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || d < 1 || num_splits < 1 || page_size < 1 || num_pages < 1 ||
+      max_pages_per_seq < 1)
+    return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH * num_splits > INT32_MAX || (long long)max_pages_per_seq * page_size > INT32_MAX)
+    return FA_ERR_SHAPE;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((page_size & (page_size - 1)) != 0 || num_splits > fa::kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_VALUE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(workspace) || ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
+    return FA_ERR_ALIGN;
+
+  fa::DecodeParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)BH;
+  p.Nk = 0;     // per sequence: seq_lens
+  p.S = num_splits;
+  p.chunk = 0;  // per sequence: ceil(seq_lens[b] / S)
+  p.c = scale * fa::kLog2e;
+  p.ws_o = (float*)workspace;
+  p.ws_ml = p.ws_o + (size_t)BH * num_splits * d;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.H = H;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  p.page_shift = shift;
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  return finish_launch(fa::launch_decode_paged(p, d, dtype == FA_BF16, (hipStream_t)stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {

@@ -18,6 +18,14 @@
 //   are merged through LDS and written to the workspace (o unnormalised, m in log2 units).
 // Kernel 2 (merge): one workgroup per (b, h), thread = output dimension; merges the S
 //   partials in split order (deterministic) and writes O = o/l and LSE = ln2*(m + log2 l).
+//
+// Paged cache (PAGED = true): the keys of sequence b live in fixed-size pages of a shared
+// pool, [num_pages][page_size][H][d], found through the sequence's block table; the same
+// page indirection that engines pair with split-KV decoding (same section of "FlashAttention:
+// Attention Is Limited by Memory, Not Math"). Each lane looks up the page of each of its
+// keys, then loads the key's row from that page; a page id outside the pool is never read
+// through and its keys are skipped. Sequence lengths may differ: each sequence's keys are
+// split into S chunks of its own.
 #include "fa_internal.h"
 
 namespace fa {
@@ -52,7 +60,7 @@ struct Elem<float> {
   }
 };
 
-template <int D, typename E>
+template <int D, typename E, bool PAGED>
 __global__ __launch_bounds__(kNT) void decode_split_kernel(DecodeParams p) {
   constexpr int VEC = Elem<E>::VEC;
   constexpr int LPK = D / VEC;    // lanes per key row
@@ -66,11 +74,24 @@ __global__ __launch_bounds__(kNT) void decode_split_kernel(DecodeParams p) {
   const int grp = tid / LPK;  // which lane group
   const int sidx = blockIdx.x % p.S;
   const int bh = blockIdx.x / p.S;
-  const int lo = sidx * p.chunk;
-  const int hi = min(p.Nk, lo + p.chunk);
-
-  const E* __restrict__ kh = (const E*)p.k + (size_t)bh * p.Nk * D;
-  const E* __restrict__ vh = (const E*)p.v + (size_t)bh * p.Nk * D;
+  int len = p.Nk, chunk = p.chunk;
+  const E* __restrict__ kh;
+  const E* __restrict__ vh;
+  const int* __restrict__ tab = nullptr;
+  if (PAGED) {
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    len = min(max(p.seq_lens[b], 0), p.max_pages << p.page_shift);
+    chunk = (len + p.S - 1) / p.S;
+    kh = (const E*)p.k + (size_t)h * D;  // row r of the pool: + r * H * D
+    vh = (const E*)p.v + (size_t)h * D;
+    tab = p.block_table + (size_t)b * p.max_pages;
+  } else {
+    kh = (const E*)p.k + (size_t)bh * p.Nk * D;
+    vh = (const E*)p.v + (size_t)bh * p.Nk * D;
+  }
+  const int lo = sidx * chunk;
+  const int hi = min(len, lo + chunk);
   float qv[VEC];
   Elem<E>::widen(*(const uint4*)((const E*)p.q + (size_t)bh * D + sub * VEC), qv);
 
@@ -82,13 +103,27 @@ __global__ __launch_bounds__(kNT) void decode_split_kernel(DecodeParams p) {
   // every thread runs the same trip count; a group's kU keys are base + u*KPI + grp
   for (int base = lo; base < hi; base += KPI * kU) {
     uint4 kx[kU], vx[kU];
+    bool ok[kU];
+    size_t row[kU];  // element offset of the key's row from kh / vh
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int key = base + u * KPI + grp;
-      if (key < hi) {
+      ok[u] = key < hi;
+      if (PAGED) {
+        const int page = ok[u] ? tab[key >> p.page_shift] : 0;
+        ok[u] = ok[u] && (unsigned)page < (unsigned)p.num_pages;
+        const size_t r = ((size_t)page << p.page_shift) | (size_t)(key & ((1 << p.page_shift) - 1));
+        row[u] = r * (size_t)p.H * D;
+      } else {
+        row[u] = (size_t)key * D;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (ok[u]) {
         // streamed once: non-temporal loads keep the cache for the workspace and q
-        const v4u a = __builtin_nontemporal_load((const v4u*)(kh + (size_t)key * D + sub * VEC));
-        const v4u b = __builtin_nontemporal_load((const v4u*)(vh + (size_t)key * D + sub * VEC));
+        const v4u a = __builtin_nontemporal_load((const v4u*)(kh + row[u] + sub * VEC));
+        const v4u b = __builtin_nontemporal_load((const v4u*)(vh + row[u] + sub * VEC));
         kx[u] = make_uint4(a[0], a[1], a[2], a[3]);
         vx[u] = make_uint4(b[0], b[1], b[2], b[3]);
       } else {
@@ -114,7 +149,7 @@ __global__ __launch_bounds__(kNT) void decode_split_kernel(DecodeParams p) {
     float bm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      s[u] = (base + u * KPI + grp < hi) ? s[u] * p.c : -INFINITY;
+      s[u] = ok[u] ? s[u] * p.c : -INFINITY;
       bm = fmaxf(bm, s[u]);
     }
     const float m_new = fmaxf(m, bm);
@@ -193,10 +228,10 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   if (dd == 0 && p.lse) p.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
-template <int D, typename E>
+template <int D, typename E, bool PAGED>
 hipError_t launch(const DecodeParams& prm, hipStream_t s) {
   DecodeParams p = prm;
-  hipLaunchKernelGGL((decode_split_kernel<D, E>), dim3(p.BH * p.S), dim3(kNT), 0, s, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, E, PAGED>), dim3(p.BH * p.S), dim3(kNT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.BH), dim3(D), 0, s, p);
@@ -206,8 +241,13 @@ hipError_t launch(const DecodeParams& prm, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s) {
-  if (bf16) return d == 128 ? launch<128, uint16_t>(p, s) : launch<64, uint16_t>(p, s);
-  return d == 128 ? launch<128, float>(p, s) : launch<64, float>(p, s);
+  if (bf16) return d == 128 ? launch<128, uint16_t, false>(p, s) : launch<64, uint16_t, false>(p, s);
+  return d == 128 ? launch<128, float, false>(p, s) : launch<64, float, false>(p, s);
+}
+
+hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s) {
+  if (bf16) return d == 128 ? launch<128, uint16_t, true>(p, s) : launch<64, uint16_t, true>(p, s);
+  return d == 128 ? launch<128, float, true>(p, s) : launch<64, float, true>(p, s);
 }
 
 }  // namespace fa

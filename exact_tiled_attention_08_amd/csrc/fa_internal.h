@@ -44,6 +44,15 @@ struct DecodeParams {
   int S;          // number of splits
   int chunk;      // keys per split, ceil(Nk / S)
   float c;        // scale * log2(e)
+  // Paged cache only (k, v are [num_pages][page_size][H][d]): key t of sequence b sits in
+  // page block_table[b][t >> page_shift], slot t & (page_size - 1); the sequence has
+  // seq_lens[b] keys, split into S chunks of ceil(seq_lens[b] / S).
+  const int* block_table;  // [B][max_pages]
+  const int* seq_lens;     // [B]
+  int H;
+  int page_shift;          // log2(page_size)
+  int max_pages;           // block table entries per sequence
+  int num_pages;           // pages in the pool; ids outside [0, num_pages) hold no keys
 };
 
 // Arguments of the backward kernels.
@@ -106,6 +115,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 // Query rows per workgroup of each prefill kernel (host needs it for the grid).

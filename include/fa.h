@@ -105,6 +105,33 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
                             void* stream);
 
 /*
+ * fa_decode_paged — fa_decode_splitkv over a paged key/value cache with per-sequence
+ * lengths: the page indirection that serving engines pair with split-KV decoding
+ * ("FlashAttention: Attention Is Limited by Memory, Not Math", section "Where it helps,
+ * and where it does not").
+ *   q        [B][H][1][d]                         dtype
+ *   k_cache, v_cache [num_pages][page_size][H][d] dtype  (a shared pool of pages)
+ *   block_table [B][max_pages_per_seq] int32 (device): key t of sequence b is row
+ *            t % page_size of page block_table[b][t / page_size].
+ *   seq_lens [B] int32 (device): keys of sequence b (clamped to [0, max_pages_per_seq *
+ *            page_size]); the single query sees all of them (it sits at the end).
+ *   o [B][H][1][d] float32, lse [B][H][1] float32 or NULL. A sequence with no key gets
+ *   O = 0 and LSE = -inf.
+ *   Each sequence's keys are cut into num_splits chunks of ceil(seq_lens[b] / num_splits);
+ *   partials merge as in fa_decode_splitkv (same workspace size:
+ *   fa_decode_workspace_bytes(B, H, d, num_splits)).
+ *   page_size: a power of two; num_pages, max_pages_per_seq >= 1. A block-table entry
+ *   outside [0, num_pages) is never read through: the keys it would hold are skipped.
+ *   block_table and seq_lens need 4-byte alignment, the other pointers 16-byte.
+ *   d in {64, 128}; FA_BF16 or FA_F32; 1 <= num_splits <= 1024.
+ */
+fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int* block_table, const int* seq_lens, float* o, float* lse,
+                          int B, int H, int d, int page_size, int num_pages, int max_pages_per_seq,
+                          float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          fa_dtype dtype, void* stream);
+
+/*
  * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs:
  * B*H*ceil(Nq/128)*128*8 (two float32 statistics per query row, rows padded to a whole
  * number of 128-row tiles). Returns 0 if an argument is < 1 or the size overflows.

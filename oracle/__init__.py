@@ -199,14 +199,15 @@ def paged_gather(cache, block_table, seq_len: int, b: int, page_size: int):
     """
     import torch
     num_pages = cache.shape[0]
-    rows = []
-    for t in range(seq_len):
-        page = int(block_table[b, t // page_size])
+    pieces = []
+    for j in range(-(-seq_len // page_size)):            # logical page j: positions j*ps ..
+        n = min(page_size, seq_len - j * page_size)
+        page = int(block_table[b, j])
         if 0 <= page < num_pages:
-            rows.append(cache[page, t % page_size])      # [H, d]
-    if not rows:
+            pieces.append(cache[page, :n])                # [n, H, d]
+    if not pieces:
         return cache.new_zeros((cache.shape[2], 0, cache.shape[3]))
-    return torch.stack(rows, dim=1).contiguous()          # [H, n, d]
+    return torch.cat(pieces, dim=0).permute(1, 0, 2).contiguous()   # [H, n, d]
 
 
 def paged_attention(q, k_cache, v_cache, block_table, seq_lens, page_size: int, scale: float,

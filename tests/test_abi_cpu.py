@@ -160,3 +160,34 @@ def test_bwd_rejects(kw, status):
 def test_bwd_lse_needs_only_word_alignment():
     # a 4-byte aligned lse passes validation up to the workspace check (which then fails)
     assert _bwd(lse=P + 4, ws=None) == fa.FA_ERR_WORKSPACE
+
+
+def _paged(**kw):
+    a = dict(q=P, kc=P, vc=P, tab=P, lens=P, o=P, lse=P, B=2, H=2, d=128, ps=16, num_pages=10,
+             max_pages=4, scale=0.1, S=4, ws=P, wsb=fa.decode_workspace_bytes(2, 2, 128, 4),
+             dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_decode_paged(a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["o"], a["lse"],
+                                        a["B"], a["H"], a["d"], a["ps"], a["num_pages"], a["max_pages"],
+                                        a["scale"], a["S"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(kc=None), fa.FA_ERR_NULL), (dict(tab=None), fa.FA_ERR_NULL),
+    (dict(lens=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(ps=0), fa.FA_ERR_SHAPE), (dict(num_pages=0), fa.FA_ERR_SHAPE),
+    (dict(max_pages=0), fa.FA_ERR_SHAPE), (dict(S=0), fa.FA_ERR_SHAPE),
+    (dict(max_pages=1 << 20, ps=1 << 12), fa.FA_ERR_SHAPE),
+    (dict(ps=12), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(S=2000, wsb=1 << 30), fa.FA_ERR_UNSUPPORTED), (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), fa.FA_ERR_VALUE),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=64), fa.FA_ERR_WORKSPACE),
+    (dict(kc=P + 8), fa.FA_ERR_ALIGN), (dict(tab=P + 2), fa.FA_ERR_ALIGN), (dict(lens=P + 1), fa.FA_ERR_ALIGN),
+])
+def test_paged_rejects(kw, status):
+    assert _paged(**kw) == status
+
+
+def test_paged_lse_may_be_null_and_tables_need_word_alignment():
+    assert _paged(lse=None, ws=None) == fa.FA_ERR_WORKSPACE   # passes up to the workspace check
+    assert _paged(tab=P + 4, lens=P + 12, ws=None) == fa.FA_ERR_WORKSPACE

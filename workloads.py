@@ -110,6 +110,24 @@ def make_grad(w: Workload, device="cpu"):
     return draw((w.B, w.H, w.Nq, w.d), 10 * w.number + 3, 1.0, w.dtype, device)
 
 
+def to_paged(k: torch.Tensor, page_size: int, seed: int):
+    """Lay a contiguous [B, H, N, d] cache out as pages: returns (cache [B*P, page_size, H, d],
+    block_table int32 [B, P]) with P = ceil(N / page_size) and the B*P pages placed in the
+    pool in a seeded random order (positions past N in the last page are zero). Data
+    movement only: the logical rows of sequence b are those of k[b]."""
+    B, H, N, d = k.shape
+    P = -(-N // page_size)
+    g = torch.Generator().manual_seed(int(seed))
+    order = torch.randperm(B * P, generator=g)
+    cache = torch.zeros((B * P, page_size, H, d), dtype=k.dtype, device=k.device)
+    for b in range(B):
+        for j in range(P):
+            n = min(page_size, N - j * page_size)
+            cache[order[b * P + j], :n] = k[b, :, j * page_size:j * page_size + n].transpose(0, 1)
+    table = order.view(B, P).to(torch.int32).to(k.device)
+    return cache, table
+
+
 def sample_rows(w: Workload, per_head: int = 64, seed: int = 12345):
     """Flat row ids (b*H + h)*Nq + i for a sampled parity check on a large workload.
 
