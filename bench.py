@@ -47,6 +47,13 @@ def traffic_for(kind: str, workload: int):
     return ent.get("bytes_per_launch")
 
 
+def bwd_traffic(workload: int):
+    """HBM bytes of one fa_bwd call: the sum over its three kernels, or None unless all three
+    were measured on the current source."""
+    parts = [traffic_for(k, workload) for k in ("bwd_pre", "bwd_dkdv", "bwd_dq")]
+    return None if any(p is None for p in parts) else sum(parts)
+
+
 def time_launches(fn, steps: int, warmup: int):
     """(wall ms per step, event ms per launch). fn launches on torch's current stream."""
     import torch
@@ -152,7 +159,7 @@ def bwd_record(num: int, steps: int, warmup: int):
         "tflops": w.bwd_flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": bwd_traffic(num)},
     }
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()

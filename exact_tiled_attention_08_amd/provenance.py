@@ -15,6 +15,9 @@ KERNEL_SOURCES = {
     "fwd_bf16": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
     "fwd_f32": ["csrc/fa_fwd_f32.hip", "csrc/fa_internal.h"],
     "decode": ["csrc/fa_decode.hip", "csrc/fa_internal.h"],
+    "bwd_pre": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
+    "bwd_dkdv": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
+    "bwd_dq": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
 }
 
 
