@@ -11,7 +11,8 @@ row by row in double precision (the C source states each passage it follows);
 from the same definition by the chain rule. ``paged_attention`` is the same definition
 for one query per sequence whose keys and values live in a paged cache: it first
 gathers each sequence's logical key/value rows through its block table, then calls
-``attention``.
+``attention``. ``attention_varlen`` applies the definition to each sequence of a packed
+batch of variable-length sequences.
 """
 from __future__ import annotations
 
@@ -233,4 +234,40 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, page_size: int, 
         ob, lb = attention(q[b:b + 1], kb[None], vb[None], scale, False, threads=threads)
         o[b * H:(b + 1) * H] = ob
         lse[b * H:(b + 1) * H] = lb
+    return o, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool = False,
+                     threads: int | None = None):
+    """Float64 attention of a packed batch of variable-length sequences.
+
+    q [total_q, H, d]; k, v [total_k, H, d] (float32 or bfloat16, CPU); cu_seqlens_q and
+    cu_seqlens_k: B + 1 non-decreasing integers from 0. Sequence b's query rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 attend to its key rows cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1]-1 of the same head, and to nothing else, with the mask of
+    ``attention`` taken inside the sequence (causal: query i of a sequence of nq queries
+    and nk keys sees key j iff j <= i + nk - nq; "Explain FlashAttention ...", section
+    "Executable recurrence, with an empty-state policy": positions are absolute within
+    the sequence). Returns (o [total_q, H, d], lse [H, total_q]) float64; a query row with
+    no visible key gets O = 0 and LSE = -inf.
+    """
+    total_q, H, d = q.shape
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or cq[0] != 0 or ck[0] != 0 or cq[-1] != total_q or ck[-1] != k.shape[0]:
+        raise ValueError("cu_seqlens must start at 0 and end at the packed lengths")
+    o = np.zeros((total_q, H, d), np.float64)
+    lse = np.full((H, total_q), -np.inf, np.float64)
+    for b in range(len(cq) - 1):
+        nq, nk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        if nq < 0 or nk < 0:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        if nq == 0 or nk == 0:
+            continue  # no rows, or rows that see no key (O = 0, LSE = -inf)
+        qb = q[cq[b]:cq[b + 1]].permute(1, 0, 2)[None].contiguous()   # [1, H, nq, d]
+        kb = k[ck[b]:ck[b + 1]].permute(1, 0, 2)[None].contiguous()
+        vb = v[ck[b]:ck[b + 1]].permute(1, 0, 2)[None].contiguous()
+        ob, lb = attention(qb, kb, vb, scale, causal, threads=threads)
+        o[cq[b]:cq[b + 1]] = ob.reshape(H, nq, d).transpose(1, 0, 2)
+        lse[:, cq[b]:cq[b + 1]] = lb.reshape(H, nq)
     return o, lse
