@@ -129,6 +129,36 @@ def prefill_record(num: int, steps: int, warmup: int):
     return rec, (w, q, k, v)
 
 
+def varlen_record(steps: int, warmup: int):
+    """fa_fwd_varlen on the packed batch of 16 causal sequences of seeded lengths."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    q, k, v, cu, lens = W.make_varlen("cuda")
+    total, H, d = q.shape
+    o = torch.empty((total, H, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    scale = 1.0 / d ** 0.5
+
+    def step():
+        fa.fwd_varlen(q, k, v, cu, cu, max(lens), scale=scale, causal=True, out=o, lse=lse)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    flops = W.varlen_flops(lens)
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    rec = {
+        "workload": f"bf16 causal packed batch of {len(lens)} sequences, lengths uniform in "
+                    f"[256, 8192] (seed 60), {total} tokens, H={H} d={d}",
+        "lengths": lens, "flops_per_launch": flops, "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "tflops": flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return rec
+
+
 def bwd_record(num: int, steps: int, warmup: int):
     """fa_bwd over workload `num` with the seeded dO; o and lse from fa_fwd (not timed)."""
     import torch
@@ -253,7 +283,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen"],
+                    default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
     args = ap.parse_args()
@@ -273,6 +304,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps({"copy": copy_record(args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "varlen":
+        print(json.dumps({"prefill_varlen": varlen_record(args.steps, args.warmup)}), flush=True)
         return
     if args.only == "paged":
         print(json.dumps({"decode_paged": paged_decode_record(args.steps, args.warmup)}), flush=True)
@@ -312,6 +346,7 @@ def main():
         rec4, _ = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
         extra["prefill_N30000"] = rec4
         torch.cuda.empty_cache()
+        extra["prefill_varlen"] = varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
         extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))
         extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))

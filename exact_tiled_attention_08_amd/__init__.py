@@ -6,6 +6,7 @@ There is no CPU or PyTorch fallback: if the library is missing, or a tensor is
 not on the GPU, the call raises.
 
     o, lse = fwd(q, k, v, scale=None, causal=False)        # prefill
+    o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)  # packed batch
     o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
     o, lse = decode_paged(q, k_cache, v_cache, block_table, seq_lens)  # paged cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, scale=None, causal=False)   # gradients
@@ -19,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
+__all__ = ["fwd", "fwd_varlen", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
            "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
@@ -31,13 +32,15 @@ FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                           _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
@@ -164,6 +167,41 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
                           B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
                           _stream_ptr(q.device))
     _raise(st, "fa_fwd")
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: float | None = None,
+               causal: bool = False, out=None, lse=None):
+    """Attention forward over a packed batch of variable-length sequences: q [total_q, H, d],
+    k, v [total_k, H, d] (bfloat16), cu_seqlens_* int32 [B+1] on the GPU. Returns
+    (o [total_q, H, d] float32, lse [H, total_q] float32)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("q must be [total_q, H, d] and k, v [total_k, H, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 \
+            or cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [B + 1]")
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((total_q, H, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    st = library().fa_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k,
+        int(max_seqlen_q), d, float(scale), int(bool(causal)), _dtype_code(q),
+        _stream_ptr(q.device))
+    _raise(st, "fa_fwd_varlen")
     return out, lse
 
 

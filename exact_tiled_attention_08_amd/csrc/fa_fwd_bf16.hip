@@ -35,6 +35,12 @@
 // matrix core busy, the other group's waves use its vector ALU. Group 0 issues the direct
 // loads of K tiles and group 1 those of V tiles, each two phases ahead of the first use.
 //
+// Packed variable-length batches (VARLEN): the same kernel over [total][H][d] tensors with
+// per-sequence row offsets; a workgroup finds its sequence's rows and lengths, exits at
+// once when its query tile lies past the sequence's end, and otherwise runs unchanged with
+// a row stride of H*d elements (masks use positions inside the sequence). Its (b, h) pairs
+// are numbered head-major so that every XCD gets a share of every sequence.
+//
 // Rescaling: the offset is always the exact running max, so the largest weight of a row
 // is exactly 1 and survives the rounding of P to bfloat16 without error (an offset that
 // lags the max would leave the dominant weight at 2^delta, rounded by up to 2^-9 of its
@@ -95,7 +101,7 @@ __device__ __forceinline__ float wave_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D, BC>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -113,27 +119,58 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + col;   // this lane's query row
 
-  const uint16_t* __restrict__ qh = (const uint16_t*)p.q + (size_t)bh * p.Nq * D;
-  const uint16_t* __restrict__ kh = (const uint16_t*)p.k + (size_t)bh * p.Nk * D;
-  const uint16_t* __restrict__ vh = (const uint16_t*)p.v + (size_t)bh * p.Nk * D;
+  // Rows of this (b, h): Nq queries and Nk keys, `rs` elements apart (a dense [B][H][N][d]
+  // tensor: d; a packed [total][H][d] batch: H*d). Causal offset off = Nk - Nq.
+  int Nq = p.Nq, Nk = p.Nk, off = p.off;
+  const uint16_t* __restrict__ qh;
+  const uint16_t* __restrict__ kh;
+  const uint16_t* __restrict__ vh;
+  float* __restrict__ oh;
+  float* __restrict__ lh;
+  if (VARLEN) {
+    // pairs are numbered head-major (h * B + b): the contiguous run of pairs that the block
+    // map gives one XCD then spans every sequence for a few heads, so the XCDs get equal
+    // work however unequal the sequences are, and a head's K/V still stays in one L2
+    const int h = bh / p.B;
+    const int b = bh - h * p.B;
+    // offsets clamped into the packed tensors, so malformed ones cannot read outside them
+    const int qs = min(max(p.cu_q[b], 0), p.total_q);
+    const int ks = min(max(p.cu_k[b], 0), p.total_k);
+    Nq = min(max(p.cu_q[b + 1], qs), p.total_q) - qs;
+    Nk = min(max(p.cu_k[b + 1], ks), p.total_k) - ks;
+    off = Nk - Nq;
+    if (q0 >= Nq) return;  // the whole workgroup: this sequence has no rows in this tile
+    qh = (const uint16_t*)p.q + ((size_t)qs * p.H + h) * D;
+    kh = (const uint16_t*)p.k + ((size_t)ks * p.H + h) * D;
+    vh = (const uint16_t*)p.v + ((size_t)ks * p.H + h) * D;
+    oh = p.o + ((size_t)qs * p.H + h) * D;
+    lh = p.lse ? p.lse + (size_t)h * p.total_q + qs : nullptr;
+  } else {
+    qh = (const uint16_t*)p.q + (size_t)bh * Nq * D;
+    kh = (const uint16_t*)p.k + (size_t)bh * Nk * D;
+    vh = (const uint16_t*)p.v + (size_t)bh * Nk * D;
+    oh = p.o + (size_t)bh * Nq * D;
+    lh = p.lse ? p.lse + (size_t)bh * Nq : nullptr;
+  }
+  const int rs = VARLEN ? p.H * D : D;  // elements between consecutive rows
 
   // Q tile stays in VGPRs for the whole key loop, as the B operand of S^T = K Q^T.
   bf16x8 qb[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    if (qrow < p.Nq)
-      qb[kk] = *(const bf16x8*)(qh + (size_t)qrow * D + 16 * kk + 8 * g);
+    if (qrow < Nq)
+      qb[kk] = *(const bf16x8*)(qh + (size_t)qrow * rs + 16 * kk + 8 * g);
     else
       qb[kk] = bf16x8{};
   }
 
   // Key tiles this workgroup visits, and the key bound of this wave (causal).
-  int kv_end = p.Nk;
-  int wave_kv_end = (wq0 < p.Nq) ? p.Nk : 0;
+  int kv_end = Nk;
+  int wave_kv_end = (wq0 < Nq) ? Nk : 0;
   if (CAUSAL) {
-    const int last_q = min(q0 + C::BR, p.Nq) - 1;
-    kv_end = min(p.Nk, last_q + p.off + 1);
-    if (wq0 < p.Nq) wave_kv_end = min(p.Nk, min(wq0 + 31, p.Nq - 1) + p.off + 1);
+    const int last_q = min(q0 + C::BR, Nq) - 1;
+    kv_end = min(Nk, last_q + off + 1);
+    if (wq0 < Nq) wave_kv_end = min(Nk, min(wq0 + 31, Nq - 1) + off + 1);
   }
   const int ntiles = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
@@ -157,8 +194,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   auto dma = [&](int t, char* dst, int n) {
     const int kv0 = t * BC;
     const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * wg4) * 16));
-    const int row = min(lrow + n * C::ROWSTEP, p.Nk - 1 - kv0);
-    dma16((const char*)lbase + (size_t)kv0 * C::ROWB, (uint32_t)(row * C::ROWB) + lchunk, lds);
+    const int row = min(lrow + n * C::ROWSTEP, Nk - 1 - kv0);
+    dma16((const char*)lbase + (size_t)kv0 * rs * 2, (uint32_t)(row * rs * 2) + lchunk, lds);
   };
   auto issue = [&](int t, char* dst) {
 #pragma unroll
@@ -176,10 +213,10 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // key kv0 + 32kb + 8(i/4) + 4g + i%4 is visible iff its in-tile offset <= lim.
   auto needs_mask = [&](int t) {
     const int kv0 = t * BC;
-    return (kv0 + BC > p.Nk) || (CAUSAL && kv0 + BC - 1 > wq0 + p.off) || (kv0 >= wave_kv_end);
+    return (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > wq0 + off) || (kv0 >= wave_kv_end);
   };
   auto mask_s = [&](int t, f32x16 (&s)[BC / 32]) {
-    const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - t * BC - 4 * g;
+    const int lim = (CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1) - t * BC - 4 * g;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -344,9 +381,9 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // Epilogue: divide by l once; LSE = ln2 * (m + log2 l). Empty row: O = 0, LSE = -inf.
   const float lt = wave_half_sum(l);
-  if (qrow < p.Nq) {
+  if (qrow < Nq) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float* orow = p.o + ((size_t)bh * p.Nq + qrow) * D;
+    float* orow = oh + (size_t)qrow * rs;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -358,19 +395,18 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
         val[3] = oacc[db][4 * j + 3] * inv;
         *(f32x4*)(orow + 32 * db + 8 * j + 4 * g) = val;
       }
-    if (g == 0 && p.lse)
-      p.lse[(size_t)bh * p.Nq + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    if (g == 0 && lh) lh[qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, int BC>
+template <int D, int BC, bool VARLEN>
 hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
   FwdParams p = prm;
   const int total = p.BH * p.nqt;
   if (causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true>), dim3(total), dim3(64 * kNW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true, VARLEN>), dim3(total), dim3(64 * kNW), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false>), dim3(total), dim3(64 * kNW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false, VARLEN>), dim3(total), dim3(64 * kNW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -379,8 +415,13 @@ hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
 int fwd_bf16_block_rows(int) { return 32 * kNW; }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s) {
-  if (d == 128) return launch<128, 96>(p, causal, s);
-  return launch<64, 128>(p, causal, s);
+  if (d == 128) return launch<128, 96, false>(p, causal, s);
+  return launch<64, 128, false>(p, causal, s);
+}
+
+hipError_t launch_fwd_bf16_varlen(const FwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return launch<128, 96, true>(p, causal, s);
+  return launch<64, 128, true>(p, causal, s);
 }
 
 }  // namespace fa

@@ -29,6 +29,14 @@ struct FwdParams {
   int nqt;        // number of query tiles per (b, h)
   int hpg;        // (b, h) pairs per XCD group for the block -> tile mapping
   float c;        // scale * log2(e): scores are exponentiated base 2
+  // Packed variable-length batches only: q, k, v, o are [total][H][d], lse [H][total_q];
+  // sequence b owns rows cu_q[b] .. cu_q[b+1]-1 (queries) and cu_k[b] .. cu_k[b+1]-1 (keys).
+  const int* cu_q;
+  const int* cu_k;
+  int B;
+  int H;
+  int total_q;
+  int total_k;
 };
 
 struct DecodeParams {
@@ -113,6 +121,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 
 // Launchers (defined next to their kernels). Each returns the hipError_t of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_fwd_bf16_varlen(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s);

@@ -80,6 +80,27 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
                  fa_dtype dtype, void* stream);
 
 /*
+ * fa_fwd_varlen — fa_fwd over a packed batch of variable-length sequences (no padding).
+ *   q [total_q][H][d], k, v [total_k][H][d]  FA_BF16     o [total_q][H][d] float32
+ *   lse [H][total_q] float32 or NULL
+ *   cu_seqlens_q, cu_seqlens_k [B+1] int32 (device): sequence b owns query rows
+ *   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ *   cu_seqlens_k[b+1]-1; both start at 0, never decrease and end at total_q / total_k.
+ *   A sequence's queries see only its own keys; the causal mask uses positions inside the
+ *   sequence, bottom-right aligned as in fa_fwd (query i of nq sees key j of nk iff
+ *   j <= i + nk - nq); a query row that sees no key gets O = 0 and LSE = -inf.
+ *   max_seqlen_q: an upper bound on every sequence's query count (rows past it are not
+ *   computed). Offsets outside [0, total] are clamped on the device, so malformed ones
+ *   cannot read or write outside the tensors.
+ *   d in {64, 128}; H*d*256 < 2^31; scale finite and > 0; causal 0 or 1. The
+ *   cu_seqlens arrays need 4-byte alignment, the tensors 16-byte.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int total_q, int total_k, int max_seqlen_q, int d, float scale,
+                        int causal, fa_dtype dtype, void* stream);
+
+/*
  * fa_decode_workspace_bytes — bytes of device workspace fa_decode_splitkv needs:
  * B*H*num_splits*(d+2)*4. Returns 0 if an argument is < 1 or the size overflows.
  */

@@ -191,3 +191,26 @@ def test_paged_rejects(kw, status):
 def test_paged_lse_may_be_null_and_tables_need_word_alignment():
     assert _paged(lse=None, ws=None) == fa.FA_ERR_WORKSPACE   # passes up to the workspace check
     assert _paged(tab=P + 4, lens=P + 12, ws=None) == fa.FA_ERR_WORKSPACE
+
+
+def _varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=2, H=4, tq=100, tk=120, maxq=60, d=128,
+             scale=0.1, causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                      a["B"], a["H"], a["tq"], a["tk"], a["maxq"], a["d"], a["scale"],
+                                      a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL), (dict(cq=None), fa.FA_ERR_NULL),
+    (dict(ck=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(tq=0), fa.FA_ERR_SHAPE), (dict(tk=0), fa.FA_ERR_SHAPE),
+    (dict(maxq=0), fa.FA_ERR_SHAPE),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=1 << 16), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(causal=3), fa.FA_ERR_VALUE),
+    (dict(q=P + 8), fa.FA_ERR_ALIGN), (dict(cq=P + 2), fa.FA_ERR_ALIGN),
+])
+def test_varlen_rejects(kw, status):
+    assert _varlen(**kw) == status

@@ -110,6 +110,34 @@ def make_grad(w: Workload, device="cpu"):
     return draw((w.B, w.H, w.Nq, w.d), 10 * w.number + 3, 1.0, w.dtype, device)
 
 
+VARLEN_SEQS, VARLEN_H, VARLEN_D = 16, 16, 128
+
+
+def varlen_lengths(seed: int = 60, n: int = VARLEN_SEQS, lo: int = 256, hi: int = 8192):
+    """Sequence lengths of the packed variable-length prefill: n lengths drawn uniformly
+    from [lo, hi] with a seeded CPU generator (a mix of short and long sequences)."""
+    g = torch.Generator().manual_seed(int(seed))
+    return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g)]
+
+
+def make_varlen(device="cpu", seed: int = 60):
+    """(q, k, v, cu_seqlens, lengths) of the packed variable-length prefill: bfloat16
+    N(0,1) [total, H, d] tensors, seeds seed+1, seed+2, seed+3, drawn as in `draw` with
+    the packed tensor as one slice; cu_seqlens int32 [n+1] (queries and keys alike)."""
+    lens = varlen_lengths(seed)
+    total = sum(lens)
+    shape = (1, total, VARLEN_H, VARLEN_D)
+    q, k, v = (draw(shape, seed + 1 + t, 1.0, torch.bfloat16, device)[0] for t in range(3))
+    cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0)), dtype=torch.int32, device=device)
+    return q, k, v, cu, lens
+
+
+def varlen_flops(lens, H: int = VARLEN_H, d: int = VARLEN_D, causal: bool = True) -> float:
+    """Algorithmic FLOPs of the packed prefill: 4*H*n*n*d per sequence, halved if causal."""
+    f = sum(4.0 * H * n * n * d for n in lens)
+    return f / 2 if causal else f
+
+
 def to_paged(k: torch.Tensor, page_size: int, seed: int):
     """Lay a contiguous [B, H, N, d] cache out as pages: returns (cache [B*P, page_size, H, d],
     block_table int32 [B, P]) with P = ceil(N / page_size) and the B*P pages placed in the
