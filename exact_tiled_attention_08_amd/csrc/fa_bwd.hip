@@ -16,7 +16,10 @@
 //   1. bwd_pre_kernel: D_i and LSE_i in log2 units per query row, into the workspace.
 //   2. bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h); each of its 4 waves keeps
 //      32 keys' K and V rows in VGPRs and their dK, dV in float32 accumulators while the
-//      query tiles (Q, dO and the row statistics, 64 rows each) stream through LDS.
+//      query tiles (Q, dO and the row statistics, 64 rows each) stream through LDS. Each
+//      tile is one stream of MFMAs with the fragment reads prefetched and the float32 work
+//      of one 32-query step spread between the MFMAs of the other step; masked pairs enter
+//      as S = -inf through the initial accumulator, so every tile runs the same code.
 //   3. bwd_dq_kernel: one workgroup per 128 query rows of one (b, h); each wave keeps 32
 //      rows' Q and dO in VGPRs and its dQ in float32 accumulators while 64-key K and V tiles
 //      stream through LDS. It recomputes S and dP rather than adding partial dQ from the
@@ -36,6 +39,8 @@
 //
 // Precision: P and dS are rounded to bfloat16 (nearest even) as MFMA operands; S, dP, the
 // statistics and every accumulation are float32; outputs are float32.
+#include <utility>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -216,6 +221,78 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     dv[db] = f32x16{};
   }
 
+  // One 64-query tile as a single stream of 4*NG MFMAs (NG = D/8 per group):
+  //   group 0: S and dP of query step 0 (A = Q and dO rows), alternating
+  //   group 1: S and dP of query step 1
+  //   group 2: dV^T += dO^T P and dK^T += Q^T dS of step 0 (A = transposed reads), alternating
+  //   group 3: the same for step 1
+  // The A fragment of MFMA f is read from LDS RING-1 MFMAs ahead. The float32 work of step 0
+  // (P = exp2(S c - LSE2), dS = P (dP - D), rounding to bfloat16) is spread over group 1's
+  // MFMAs and that of step 1 over group 2's, so the matrix core and the vector ALU of the
+  // SIMD work at the same time.
+  auto plain_tile = [&](const char* Qs, const char* dOs, const float* sts, const f32x16 (&sinit)[2]) {
+    constexpr int NG = D / 8, NF = 4 * NG, RING = 6, EPM = 16 / NG;  // elements per MFMA
+    f32x16 s[2], dp[2];
+    bf16x8 pb[2][2], dsb[2][2];
+    f32x4 L[2], Dv[2];  // LSE2 and D of one group of 4 elements, double-buffered
+    bf16x8 fr[RING];
+    auto frag = [&](auto fc) -> bf16x8 {
+      constexpr int f = decltype(fc)::value, x = (f / NG) & 1, i = f % NG;
+      if constexpr (f < 2 * NG) {
+        return rfrag<D>((i & 1) ? dOs : Qs, 32 * x + col, 2 * (i >> 1) + g);
+      } else {
+        constexpr int st = i / (NG / 2), db = (i % (NG / 2)) >> 1;
+        return tfrag<D>((i & 1) ? Qs : dOs, 32 * x + 16 * st, db, lane);
+      }
+    };
+    // statistics of elements 4j..4j+3 of step x (queries 32x + 8j + 4g + 0..3)
+    auto stats = [&](int x, int j) {
+      L[j & 1] = *(const f32x4*)(sts + 32 * x + 8 * j + 4 * g);
+      Dv[j & 1] = *(const f32x4*)(sts + 64 + 32 * x + 8 * j + 4 * g);
+    };
+    auto elem = [&](auto xc, auto ec) {
+      constexpr int x = decltype(xc)::value, e = decltype(ec)::value;
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x][e], p.c, -L[(e >> 2) & 1][e & 3]));
+      const float ds = pe * (dp[x][e] - Dv[(e >> 2) & 1][e & 3]);
+      pb[x][e >> 3][e & 7] = (__bf16)pe;
+      dsb[x][e >> 3][e & 7] = (__bf16)ds;
+    };
+    auto step = [&](auto fc) {
+      constexpr int f = decltype(fc)::value, grp = f / NG, i = f % NG;
+      if constexpr (f + RING - 1 < NF) fr[(f + RING - 1) % RING] = frag(std::integral_constant<int, f + RING - 1>{});
+      // statistics one group of 4 elements ahead of the element work (MPG MFMAs per group)
+      constexpr int MPG = 4 / EPM;
+      if constexpr (f == NG - MPG) stats(0, 0);
+      if constexpr ((grp == 1 || grp == 2) && i % MPG == 0 && i / MPG + 1 < 4) stats(grp - 1, i / MPG + 1);
+      if constexpr (f == 2 * NG - MPG) stats(1, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this MFMA
+      if constexpr (grp < 2) {
+        constexpr int kk = i >> 1;
+        if constexpr (i & 1)
+          dp[grp] = mfma(fr[f % RING], vf[kk], kk == 0 ? f32x16{} : dp[grp]);
+        else
+          s[grp] = mfma(fr[f % RING], kf[kk], kk == 0 ? sinit[grp] : s[grp]);
+      } else {
+        constexpr int x = grp - 2, st = i / (NG / 2), db = (i % (NG / 2)) >> 1;
+        if constexpr (i & 1)
+          dk[db] = mfma(fr[f % RING], dsb[x][st], dk[db]);
+        else
+          dv[db] = mfma(fr[f % RING], pb[x][st], dv[db]);
+      }
+      if constexpr (grp == 1 || grp == 2) {
+        [&]<int... E>(std::integer_sequence<int, E...>) {
+          (elem(std::integral_constant<int, grp - 1>{}, std::integral_constant<int, EPM * i + E>{}), ...);
+        }(std::make_integer_sequence<int, EPM>{});
+      }
+    };
+    [&]<int... F>(std::integer_sequence<int, F...>) {
+      ((fr[F] = frag(std::integral_constant<int, F>{})), ...);
+    }(std::make_integer_sequence<int, RING - 1>{});
+    [&]<int... F>(std::integer_sequence<int, F...>) {
+      (step(std::integral_constant<int, F>{}), ...);
+    }(std::make_integer_sequence<int, NF>{});
+  };
+
   if (t0 < t1) issue(t0, stage(0));
   for (int t = t0; t < t1; ++t) {
     const int cur = (t - t0) & 1;
@@ -225,46 +302,23 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     const char* Qs = stage(cur);
     const char* dOs = Qs + C::TILEB;
     const float* sts = (const float*)(Qs + 2 * C::TILEB);
+    const int qa0 = t * kRows;
+    // no query of this tile sees a key of this wave (causal): nothing to add
+    if (CAUSAL && qa0 + kRows - 1 + p.off < kw0) continue;
+    // Masked pairs enter as S = -inf through the initial accumulator of the S product, so
+    // that P = exp2(-inf) = 0 and dS = 0 with no extra work in the stream; element e of
+    // step x is query qa0 + 32x + 8(e/4) + 4g + e%4 and is masked iff key > query + off.
+    // Query rows past Nq need no mask: their LSE2 is +inf.
+    f32x16 sinit[2] = {f32x16{}, f32x16{}};
+    if (CAUSAL && qa0 + p.off < kw0 + 31) {  // the tile's first query misses a key
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int qa = t * kRows + 32 * qs;  // first query of this 32-row step
-      if (qa >= p.Nq) continue;           // padding rows only
-      if (CAUSAL && qa + 31 + p.off < kw0) continue;  // no query here sees a key of this wave
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int x = 0; x < 2; ++x) {
+        const int lim = key - p.off - qa0 - 32 * x - 4 * g;  // visible iff 8(e/4) + e%4 >= lim
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma(rfrag<D>(Qs, 32 * qs + col, 2 * kk + g), kf[kk], s);
-        dp = mfma(rfrag<D>(dOs, 32 * qs + col, 2 * kk + g), vf[kk], dp);
+        for (int e = 0; e < 16; ++e) sinit[x][e] = (8 * (e >> 2) + (e & 3) < lim) ? -INFINITY : 0.f;
       }
-      // element i of this lane: query qa + 8(i/4) + 4g + i%4, key `key`
-      const bool need_mask = CAUSAL && (qa + p.off < kw0 + 31);
-      const int lim = key - p.off - qa - 4 * g;  // visible iff 8(i/4) + i%4 >= lim
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *(const f32x4*)(sts + 32 * qs + 8 * j + 4 * g);
-        const f32x4 d4 = *(const f32x4*)(sts + 64 + 32 * qs + 8 * j + 4 * g);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * j + u;
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -l4[u]));
-          if (need_mask && 8 * j + u < lim) pe = 0.f;
-          const float ds = pe * (dp[i] - d4[u]);
-          pb[i >> 3][i & 7] = (__bf16)pe;
-          dsb[i >> 3][i & 7] = (__bf16)ds;
-        }
-      }
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dv[db] = mfma(tfrag<D>(dOs, 32 * qs + 16 * st2, db, lane), pb[st2], dv[db]);
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dk[db] = mfma(tfrag<D>(Qs, 32 * qs + 16 * st2, db, lane), dsb[st2], dk[db]);
     }
+    plain_tile(Qs, dOs, sts, sinit);
   }
 
   // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4.
