@@ -101,9 +101,21 @@ def _as_input(x):
     raise TypeError(f"oracle inputs must be float32 or raw bfloat16 (uint16), got {x.dtype}")
 
 
+def _causal_code(causal) -> int:
+    """0 = no mask, 1 (or True) = causal with the queries at the end of the key sequence
+    (bottom-right), 2 = causal with the queries at its start (top-left)."""
+    c = int(causal)
+    if c not in (0, 1, 2):
+        raise ValueError("causal must be 0/False, 1/True (bottom-right) or 2 (top-left)")
+    return c
+
+
 def attention(q, k, v, scale: float, causal: bool = False, rows=None,
               want_p: bool = False, threads: int | None = None):
     """Float64 attention for q [B,H,Nq,d], k/v [B,H,Nk,d] (float32 or bfloat16).
+
+    ``causal``: 0/False none; 1/True the query rows are the last Nq key positions (query i
+    sees key j iff j <= i + Nk - Nq); 2 they are the first Nq (j <= i).
 
     ``rows``: optional flat row ids (b*H + h)*Nq + i to evaluate (sampled
     checks); default all rows. ``scale`` is used as the exact double given;
@@ -134,7 +146,7 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
     scratch = np.empty((threads, Nk), np.float64)
     rc = _load().oracle_attention(
         qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, B, H, Nq, Nk, d,
-        float(scale), int(bool(causal)),
+        float(scale), _causal_code(causal),
         rows_arr.ctypes.data if rows_arr is not None else None, nrows, threads,
         scratch.ctypes.data, o.ctypes.data, lse.ctypes.data,
         p.ctypes.data if p is not None else None)
@@ -179,7 +191,7 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, qrows=None, k
     dv = np.empty((nk, d), np.float64)
     rc = _load().oracle_attention_bwd(
         qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, dt, B, H, Nq, Nk, d,
-        float(scale), int(bool(causal)),
+        float(scale), _causal_code(causal),
         qr.ctypes.data if qr is not None else None, nq,
         kr.ctypes.data if kr is not None else None, nk, threads,
         dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)

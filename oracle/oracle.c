@@ -25,8 +25,10 @@
  *     empty-state policy" (last paragraph) and section "Common mistakes".
  *     Reading taken where the pages are silent: when Nq != Nk the query rows
  *     are the LAST Nq positions of the key sequence (bottom-right
- *     alignment), so query i sits at absolute position i + (Nk - Nq) and sees
- *     key j iff j <= i + (Nk - Nq).
+ *     alignment, causal = 1), so query i sits at absolute position
+ *     i + (Nk - Nq) and sees key j iff j <= i + (Nk - Nq). The other reading,
+ *     queries at the FIRST Nq positions (top-left, causal = 2: query i sees
+ *     key j iff j <= i), is offered as an option. For Nq == Nk both are j <= i.
  *   - A row with no visible key returns O = 0: same page and section (the
  *     explicit empty-row policy). Its log-sum-exp is -inf (the log of an
  *     empty sum).
@@ -56,6 +58,13 @@ static double widen(const void* base, int dtype, size_t idx) {
   return (double)f;
 }
 
+/* Key position of query row 0 under the causal mask: bottom-right (causal = 1)
+ * places the queries at the end of the key sequence, top-left (causal = 2) at its
+ * start. */
+static long long query_offset(int causal, int Nq, int Nk) {
+  return causal == 2 ? 0 : (long long)Nk - (long long)Nq;
+}
+
 /*
  * One query row: row id r = (b*H + h)*Nq + i.
  * s   : scratch of Nk doubles (scores, then unnormalised weights)
@@ -68,7 +77,7 @@ static void one_row(const void* q, const void* k, const void* v, int dtype,
   int i = (int)(r % Nq);
   size_t qoff = (size_t)r * (size_t)d;
   size_t kvbase = (size_t)bh * (size_t)Nk * (size_t)d;
-  long long last_visible = causal ? (long long)i + (long long)(Nk - Nq) : (long long)Nk - 1;
+  long long last_visible = causal ? (long long)i + query_offset(causal, Nq, Nk) : (long long)Nk - 1;
   (void)H;
 
   /* scores of visible keys; masked keys are -inf */
@@ -124,6 +133,7 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
   if (!q || !k || !v || !o || !lse || !scratch) return -1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (causal < 0 || causal > 2) return -1;
   long long total = (long long)B * H * Nq;
   if (!rows) nrows = total;
   for (long long n = 0; rows && n < nrows; ++n)
@@ -184,7 +194,7 @@ static double score(const void* q, const void* k, int dtype, int Nq, int Nk, int
                     double scale, int causal, long long r, int j) {
   long long bh = r / Nq;
   int i = (int)(r % Nq);
-  if (causal && (long long)j - (long long)(Nk - Nq) > (long long)i) return -INFINITY;
+  if (causal && (long long)j - query_offset(causal, Nq, Nk) > (long long)i) return -INFINITY;
   size_t qoff = (size_t)r * d, koff = ((size_t)bh * Nk + j) * d;
   double dot = 0.0;
   for (int t = 0; t < d; ++t) dot += widen(q, dtype, qoff + t) * widen(k, dtype, koff + t);
@@ -219,6 +229,7 @@ int oracle_attention_bwd(const void* q, const void* k, const void* v, const void
   if (!q || !k || !v || !dout) return -1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (causal < 0 || causal > 2) return -1;
   const long long BH = (long long)B * H;
   if (!qrows) nq = BH * Nq;
   if (!krows) nk = BH * Nk;

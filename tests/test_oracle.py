@@ -132,12 +132,13 @@ def test_worked_example_two_tiles_interview():
 
 # ---------------------------------------------------------------- closed forms
 
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal", [False, True, 2])
 @pytest.mark.parametrize("nq,nk", [(7, 7), (5, 9), (9, 5), (1, 33)])
 def test_uniform_scores_give_mean_of_visible_values(causal, nq, nk):
     """q = 0 makes every visible score 0, so softmax is uniform over visible keys: O is the
     mean of the visible value rows and LSE = ln(count). With causal masking query i sees
-    keys 0..i+(Nk-Nq), which pins the absolute-position offset."""
+    keys 0..i+(Nk-Nq) (bottom-right, causal = 1) or 0..i (top-left, causal = 2), which pins
+    the absolute-position offset of each alignment."""
     rng = np.random.default_rng(3)
     d = 6
     q = np.zeros((2, 3, nq, d), np.float32)
@@ -149,7 +150,11 @@ def test_uniform_scores_give_mean_of_visible_values(causal, nq, nk):
     for b in range(2):
         for h in range(3):
             for i in range(nq):
-                n = min(nk, i + (nk - nq) + 1) if causal else nk
+                n = nk
+                if causal == 2:
+                    n = min(nk, i + 1)
+                elif causal:
+                    n = min(nk, i + (nk - nq) + 1)
                 if n <= 0:
                     assert np.all(o[b, h, i] == 0.0) and lse[b, h, i] == -math.inf
                     continue
@@ -242,7 +247,7 @@ def _brute_row(qi, kk, vv, scale, last):
     return out, math.log(tot)
 
 
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal", [False, True, 2])
 @pytest.mark.parametrize("nq,nk,d", [(5, 5, 3), (3, 11, 8), (13, 4, 2), (16, 16, 7), (1, 9, 4)])
 def test_brute_force_tiny(causal, nq, nk, d):
     rng = np.random.default_rng(100 + nq * 7 + nk + d)
@@ -255,7 +260,11 @@ def test_brute_force_tiny(causal, nq, nk, d):
     for b in range(B):
         for h in range(H):
             for i in range(nq):
-                last = min(nk - 1, i + nk - nq) if causal else nk - 1
+                last = nk - 1
+                if causal == 2:
+                    last = min(nk - 1, i)
+                elif causal:
+                    last = min(nk - 1, i + nk - nq)
                 want, wl = _brute_row(q[b, h, i], k[b, h], v[b, h], scale, last)
                 assert np.max(np.abs(o[b, h, i] - np.array(want))) <= 1e-13
                 if wl == -math.inf:

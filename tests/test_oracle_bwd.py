@@ -38,7 +38,7 @@ def _loss(q, k, v, do, scale, causal):
     return float((o * do.double().reshape(-1, q.shape[-1]).numpy()).sum())
 
 
-@pytest.mark.parametrize("causal,Nq,Nk", [(False, 5, 7), (True, 6, 6), (True, 4, 9)])
+@pytest.mark.parametrize("causal,Nq,Nk", [(False, 5, 7), (True, 6, 6), (True, 4, 9), (2, 4, 9), (2, 9, 4)])
 def test_finite_differences(causal, Nq, Nk):
     B, H, d, scale = 1, 2, 4, 0.7
     q, k, v, do = _inputs(B, H, Nq, Nk, d, seed=11)

@@ -30,7 +30,7 @@ MUTANTS = {
     "dP from the query row": ("size_t ooff = (size_t)r * d, voff = ((size_t)bh * Nk + j) * d;",
                               "size_t ooff = (size_t)r * d, voff = (size_t)r * d;"),
     "causal mask ignored in the gradient":
-        ("if (causal && (long long)j - (long long)(Nk - Nq) > (long long)i) return -INFINITY;",
+        ("if (causal && (long long)j - query_offset(causal, Nq, Nk) > (long long)i) return -INFINITY;",
          "(void)i;"),
 }
 

@@ -14,7 +14,11 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
     "no max subtraction": ("exp(s[j] - m)", "exp(s[j])"),
-    "causal ignores the Nk-Nq offset": ("(long long)i + (long long)(Nk - Nq)", "(long long)i"),
+    "causal ignores the Nk-Nq offset": ("(long long)i + query_offset(causal, Nq, Nk)", "(long long)i"),
+    "top-left alignment uses the bottom-right offset": ("return causal == 2 ? 0 : (long long)Nk - (long long)Nq;",
+                                                       "return (long long)Nk - (long long)Nq;"),
+    "top-left alignment shifted by one": ("return causal == 2 ? 0 : (long long)Nk - (long long)Nq;",
+                                          "return causal == 2 ? 1 : (long long)Nk - (long long)Nq;"),
     "causal off by one": ("(long long)j > last_visible", "(long long)j >= last_visible"),
     "K operand transposed": ("widen(k, dtype, kvbase + (size_t)j * d + t)",
                              "widen(k, dtype, kvbase + (size_t)t * Nk + j)"),
@@ -34,6 +38,8 @@ PINS = [
     pins.test_worked_example_two_tiles_interview,
     lambda: pins.test_uniform_scores_give_mean_of_visible_values(True, 5, 9),
     lambda: pins.test_uniform_scores_give_mean_of_visible_values(True, 9, 5),
+    lambda: pins.test_uniform_scores_give_mean_of_visible_values(2, 5, 9),
+    lambda: pins.test_brute_force_tiny(2, 13, 4, 2),
     pins.test_rows_of_p_sum_to_one_and_are_nonnegative,
     lambda: pins.test_common_shift_cancels_and_guards_overflow(1e4),
     pins.test_special_cases,
