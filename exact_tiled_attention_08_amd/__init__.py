@@ -139,6 +139,15 @@ def _check_inputs(q, k, v):
         raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
 
 
+def _causal_arg(causal) -> int:
+    """False/0: no mask; True/1: causal, queries at the end of the key sequence (bottom-right);
+    2: causal, queries at its start (top-left)."""
+    c = int(causal)
+    if c not in (0, 1, 2):
+        raise ValueError("causal must be False/0, True/1 (bottom-right) or 2 (top-left)")
+    return c
+
+
 def _stream_ptr(device):
     import torch
     return torch.cuda.current_stream(device).cuda_stream
@@ -164,7 +173,7 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr() if lse is not None else None,
-                          B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
+                          B, H, Nq, Nk, d, float(scale), _causal_arg(causal), _dtype_code(q),
                           _stream_ptr(q.device))
     _raise(st, "fa_fwd")
     return out, lse
@@ -199,7 +208,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: fl
     st = library().fa_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k,
-        int(max_seqlen_q), d, float(scale), int(bool(causal)), _dtype_code(q),
+        int(max_seqlen_q), d, float(scale), _causal_arg(causal), _dtype_code(q),
         _stream_ptr(q.device))
     _raise(st, "fa_fwd_varlen")
     return out, lse
@@ -308,7 +317,7 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, d
     st = library().fa_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d, float(scale),
-        int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _causal_arg(causal), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _dtype_code(q), _stream_ptr(q.device))
     _raise(st, "fa_bwd")
     return dq, dk, dv

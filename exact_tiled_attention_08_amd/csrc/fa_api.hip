@@ -32,6 +32,10 @@ int heads_per_group(int BH, long long nqt) {
   return (nqt > 64 && per_xcd % 2 == 0) ? 2 : per_xcd;
 }
 
+// Key position of query row 0 under the causal mask: the queries are the last Nq positions
+// of the key sequence (causal = 1, bottom-right) or the first Nq (causal = 2, top-left).
+int query_offset(int causal, int Nq, int Nk) { return causal == 2 ? 0 : Nk - Nq; }
+
 }  // namespace
 
 extern "C" {
@@ -44,7 +48,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or size";
     case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
-    case FA_ERR_VALUE: return "scale must be finite and > 0; causal must be 0 or 1";
+    case FA_ERR_VALUE: return "scale must be finite and > 0; causal must be 0, 1 or 2";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
   }
   return "unknown status";
@@ -64,7 +68,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_VALUE;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
 
   const int br = dtype == FA_BF16 ? fa::fwd_bf16_block_rows(d) : fa::fwd_f32_block_rows(d);
@@ -80,7 +84,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
   p.BH = (int)BH;
   p.Nq = Nq;
   p.Nk = Nk;
-  p.off = Nk - Nq;
+  p.off = query_offset(causal, Nq, Nk);
   p.nqt = (int)nqt;
   p.hpg = heads_per_group((int)BH, nqt);
   p.c = scale * fa::kLog2e;
@@ -102,7 +106,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, f
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // a K/V tile's rows must lie within 2^31 bytes of its first row (32-bit load offsets)
   if ((long long)H * d * 2 * 128 > INT32_MAX) return FA_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_VALUE;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       ((uintptr_t)cu_seqlens_q & 3u) != 0 || ((uintptr_t)cu_seqlens_k & 3u) != 0)
     return FA_ERR_ALIGN;
@@ -130,6 +134,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, f
   p.H = H;
   p.total_q = total_q;
   p.total_k = total_k;
+  p.top_left = causal == 2;
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   return finish_launch(fa::launch_fwd_bf16_varlen(p, d, causal != 0, (hipStream_t)stream));
 }
@@ -245,7 +250,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_VALUE;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
   const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
   if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -271,7 +276,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   p.Nq = Nq;
   p.Nk = Nk;
   p.Nq_pad = (int)(nqt * fa::kBwdQueryRows);
-  p.off = Nk - Nq;
+  p.off = query_offset(causal, Nq, Nk);
   p.nkt = (int)nkt;
   p.nqt = (int)nqt;
   p.hpg_kv = heads_per_group((int)BH, nkt);

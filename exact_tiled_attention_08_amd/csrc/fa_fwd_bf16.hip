@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   const int qrow = wq0 + col;   // this lane's query row
 
   // Rows of this (b, h): Nq queries and Nk keys, `rs` elements apart (a dense [B][H][N][d]
-  // tensor: d; a packed [total][H][d] batch: H*d). Causal offset off = Nk - Nq.
+  // tensor: d; a packed [total][H][d] batch: H*d). Causal offset: key position of query 0.
   int Nq = p.Nq, Nk = p.Nk, off = p.off;
   const uint16_t* __restrict__ qh;
   const uint16_t* __restrict__ kh;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     const int ks = min(max(p.cu_k[b], 0), p.total_k);
     Nq = min(max(p.cu_q[b + 1], qs), p.total_q) - qs;
     Nk = min(max(p.cu_k[b + 1], ks), p.total_k) - ks;
-    off = Nk - Nq;
+    off = p.top_left ? 0 : Nk - Nq;
     if (q0 >= Nq) return;  // the whole workgroup: this sequence has no rows in this tile
     qh = (const uint16_t*)p.q + ((size_t)qs * p.H + h) * D;
     kh = (const uint16_t*)p.k + ((size_t)ks * p.H + h) * D;

@@ -25,7 +25,7 @@ struct FwdParams {
   int BH;         // B * H
   int Nq;
   int Nk;
-  int off;        // Nk - Nq: absolute position of query row 0 for causal masking
+  int off;        // key position of query row 0 for causal masking (Nk - Nq or 0)
   int nqt;        // number of query tiles per (b, h)
   int hpg;        // (b, h) pairs per XCD group for the block -> tile mapping
   float c;        // scale * log2(e): scores are exponentiated base 2
@@ -37,6 +37,7 @@ struct FwdParams {
   int H;
   int total_q;
   int total_k;
+  int top_left;   // causal queries at the start of each sequence's keys (else at the end)
 };
 
 struct DecodeParams {
@@ -82,7 +83,7 @@ struct BwdParams {
   int Nq;
   int Nk;
   int Nq_pad;         // Nq rounded up to a whole number of dQ query tiles
-  int off;            // Nk - Nq
+  int off;            // key position of query row 0 for causal masking (Nk - Nq or 0)
   int nkt;            // key tiles per (b, h) of the dK/dV kernel
   int nqt;            // query tiles per (b, h) of the dQ kernel
   int hpg_kv;         // (b, h) pairs per XCD group, dK/dV kernel

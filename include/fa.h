@@ -28,12 +28,13 @@
  *     [B][H][Nq] for lse. q, k, v and o must be 16-byte aligned.
  *   - q, k, v hold FA_BF16 (bfloat16) or FA_F32 (IEEE float32) elements; o and
  *     lse are always float32.
- *   - Causal masking uses absolute positions with the query block aligned to the
- *     END of the key sequence: query i (0-based) sits at position i + (Nk - Nq)
- *     and sees key j iff j <= i + (Nk - Nq). For Nq == Nk this is j <= i.
- *     ("Explain FlashAttention ...", section "Executable recurrence, with an
- *     empty-state policy": masks use global positions, not tile-local ones.)
- *   - A query row that sees no key (only possible when causal and Nq > Nk) gets
+ *   - Causal masking uses absolute positions ("Explain FlashAttention ...",
+ *     section "Executable recurrence, with an empty-state policy": masks use global
+ *     positions, not tile-local ones). `causal` = 1 aligns the query block to the
+ *     END of the key sequence: query i (0-based) sits at position i + (Nk - Nq) and
+ *     sees key j iff j <= i + (Nk - Nq). `causal` = 2 aligns it to the START: query i
+ *     sees key j iff j <= i. For Nq == Nk both are j <= i; 0 means no mask.
+ *   - A query row that sees no key (only possible when causal = 1 and Nq > Nk) gets
  *     O = 0 and LSE = -inf (the empty-row policy of the same section).
  *   - LSE is the natural-log log-sum-exp of the scaled, masked scores of the row.
  *   - Arguments are validated before any HIP call; a rejected call launches
@@ -58,7 +59,7 @@ typedef enum {
   FA_ERR_UNSUPPORTED = -3,  /* valid but not implemented: head dim, dtype, size    */
   FA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than required             */
   FA_ERR_HIP = -5,          /* the HIP runtime reported an error at launch         */
-  FA_ERR_VALUE = -6,        /* scale not finite and > 0, causal not 0/1, ...       */
+  FA_ERR_VALUE = -6,        /* scale not finite and > 0, causal not 0/1/2, ...     */
   FA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned             */
 } fa_status;
 
@@ -71,7 +72,7 @@ typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
  *   lse [B][H][Nq]     float32 (written) or NULL to skip it
  *   d in {64, 128}; B, H, Nq, Nk >= 1 (ragged sizes allowed); Nk * d <= 2^30.
  *   scale: finite and > 0 (1/sqrt(d) for standard attention).
- *   causal: 0 or 1.
+ *   causal: 0, 1 (bottom-right) or 2 (top-left).
  * bf16 inputs use bf16 MFMA with float32 accumulation; float32 inputs use
  * float32 MFMA and never round to a narrower type.
  */
@@ -87,12 +88,13 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
  *   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
  *   cu_seqlens_k[b+1]-1; both start at 0, never decrease and end at total_q / total_k.
  *   A sequence's queries see only its own keys; the causal mask uses positions inside the
- *   sequence, bottom-right aligned as in fa_fwd (query i of nq sees key j of nk iff
- *   j <= i + nk - nq); a query row that sees no key gets O = 0 and LSE = -inf.
+ *   sequence, aligned as in fa_fwd (causal = 1: query i of nq sees key j of nk iff
+ *   j <= i + nk - nq; causal = 2: iff j <= i); a row that sees no key gets O = 0 and
+ *   LSE = -inf.
  *   max_seqlen_q: an upper bound on every sequence's query count (rows past it are not
  *   computed). Offsets outside [0, total] are clamped on the device, so malformed ones
  *   cannot read or write outside the tensors.
- *   d in {64, 128}; H*d*256 < 2^31; scale finite and > 0; causal 0 or 1. The
+ *   d in {64, 128}; H*d*256 < 2^31; scale finite and > 0; causal 0, 1 or 2. The
  *   cu_seqlens arrays need 4-byte alignment, the tensors 16-byte.
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
@@ -175,7 +177,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
  *   workspace: device memory of at least fa_bwd_workspace_bytes(B, H, Nq) bytes, 16-byte
  *   aligned, owned by the caller; contents on entry are ignored, on return unspecified.
  *   dtype: FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). d in {64, 128}; B, H, Nq, Nk >= 1;
- *   Nq * d, Nk * d <= 2^30. scale finite and > 0; causal 0 or 1 (the same alignment as
+ *   Nq * d, Nk * d <= 2^30. scale finite and > 0; causal 0, 1 or 2 (the alignments of
  *   fa_fwd). lse only needs 4-byte alignment. Three kernels run in order on `stream`;
  *   every output element is written exactly once (deterministic, no atomics). P and dS are
  *   rounded to bfloat16 as MFMA operands; everything else is float32.

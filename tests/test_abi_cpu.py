@@ -68,7 +68,7 @@ def _fwd(**kw):
     (dict(dtype=7), fa.FA_ERR_UNSUPPORTED), (dict(Nk=1 << 25, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(scale=-1.0), fa.FA_ERR_VALUE),
     (dict(scale=float("inf")), fa.FA_ERR_VALUE), (dict(scale=float("nan")), fa.FA_ERR_VALUE),
-    (dict(causal=2), fa.FA_ERR_VALUE),
+    (dict(causal=3), fa.FA_ERR_VALUE), (dict(causal=-1), fa.FA_ERR_VALUE),
     (dict(q=P + 8), fa.FA_ERR_ALIGN), (dict(k=P + 2), fa.FA_ERR_ALIGN),
     (dict(v=P + 4), fa.FA_ERR_ALIGN), (dict(o=P + 12), fa.FA_ERR_ALIGN),
 ])
