@@ -28,6 +28,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32 = 1
 BF16 = 0
+F64 = 2
 
 _lib = None
 
@@ -90,12 +91,16 @@ def _as_input(x):
                 return x.view(torch.int16).numpy().view(np.uint16), BF16
             if x.dtype == torch.float32:
                 return x.numpy(), F32
-            raise TypeError(f"oracle inputs must be float32 or bfloat16, got {x.dtype}")
+            if x.dtype == torch.float64:
+                return x.numpy(), F64
+            raise TypeError(f"oracle inputs must be float32, bfloat16 or float64, got {x.dtype}")
     except ImportError:  # pragma: no cover
         pass
     x = np.ascontiguousarray(x)
     if x.dtype == np.float32:
         return x, F32
+    if x.dtype == np.float64:
+        return x, F64
     if x.dtype == np.uint16:  # raw bfloat16 bits
         return x, BF16
     raise TypeError(f"oracle inputs must be float32 or raw bfloat16 (uint16), got {x.dtype}")
@@ -112,7 +117,8 @@ def _causal_code(causal) -> int:
 
 def attention(q, k, v, scale: float, causal: bool = False, rows=None,
               want_p: bool = False, threads: int | None = None):
-    """Float64 attention for q [B,H,Nq,d], k/v [B,H,Nk,d] (float32 or bfloat16).
+    """Float64 attention for q [B,H,Nq,d], k/v [B,H,Nk,d] (float32, bfloat16 or float64;
+    float64 carries exactly dequantized 8-bit inputs).
 
     ``causal``: 0/False none; 1/True the query rows are the last Nq key positions (query i
     sees key j iff j <= i + Nk - Nq); 2 they are the first Nq (j <= i).

@@ -37,7 +37,7 @@
  *     "Flash Attention Optimization", section "Sizing a tile, and why the
  *     backward pass recomputes instead of storing" (only m and l are kept).
  *
- * Precision: every input element (IEEE float32 or bfloat16 bit pattern) is
+ * Precision: every input element (IEEE float32, bfloat16 bit pattern or float64) is
  * widened exactly to double; all arithmetic is double with libm exp/log.
  */
 #include <math.h>
@@ -48,9 +48,11 @@
 
 #define ORACLE_F32 1
 #define ORACLE_BF16 0
+#define ORACLE_F64 2
 
-/* Widen element idx of a float32 or bfloat16 array to double (exact). */
+/* Widen element idx of a float32, bfloat16 or float64 array to double (exact). */
 static double widen(const void* base, int dtype, size_t idx) {
+  if (dtype == ORACLE_F64) return ((const double*)base)[idx];
   if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
   uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
   float f;
@@ -132,7 +134,7 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
                      double* scratch, double* o, double* lse, double* p) {
   if (!q || !k || !v || !o || !lse || !scratch) return -1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
-  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
   if (causal < 0 || causal > 2) return -1;
   long long total = (long long)B * H * Nq;
   if (!rows) nrows = total;
@@ -228,7 +230,7 @@ int oracle_attention_bwd(const void* q, const void* k, const void* v, const void
                          double* dq, double* dk, double* dv) {
   if (!q || !k || !v || !dout) return -1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
-  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
   if (causal < 0 || causal > 2) return -1;
   const long long BH = (long long)B * H;
   if (!qrows) nq = BH * Nq;
