@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak (prefill); HBM GB/s (decode)"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -127,6 +128,34 @@ def prefill_record(num: int, steps: int, warmup: int):
                      "frac": achieved / peak, "traffic": traffic_for("fwd_bf16", num)},
     }
     return rec, (w, q, k, v)
+
+
+def fp8_record(num: int, steps: int, warmup: int):
+    """fa_fwd_fp8 on workload `num`'s shape with its draws quantised per tensor to E4M3."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[num]
+    (q8, qd), (k8, kd), (v8, vd) = W.make_inputs_fp8(w, "cuda")
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    achieved = w.flops / (ev_ms * 1e-3) / 1e12
+    rec = {
+        "workload": f"{w.name}, inputs E4M3 (per-tensor descale max|x|/448)",
+        "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+        "flops_per_launch": w.flops, "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None},
+    }
+    del q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
+    return rec
 
 
 def varlen_record(steps: int, warmup: int):
@@ -283,7 +312,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen"],
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen", "fp8"],
                     default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
@@ -304,6 +333,9 @@ def main():
         return
     if args.only == "copy":
         print(json.dumps({"copy": copy_record(args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "fp8":
+        print(json.dumps({"prefill_fp8": fp8_record(args.workload, args.steps, args.warmup)}), flush=True)
         return
     if args.only == "varlen":
         print(json.dumps({"prefill_varlen": varlen_record(args.steps, args.warmup)}), flush=True)
@@ -346,6 +378,8 @@ def main():
         rec4, _ = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
         extra["prefill_N30000"] = rec4
         torch.cuda.empty_cache()
+        extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
+        extra["prefill_fp8_N30000"] = fp8_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
         extra["prefill_varlen"] = varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
         extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))

@@ -7,6 +7,7 @@ not on the GPU, the call raises.
 
     o, lse = fwd(q, k, v, scale=None, causal=False)        # prefill
     o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)  # packed batch
+    o, lse = fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale)   # E4M3 inputs
     o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
     o, lse = decode_paged(q, k_cache, v_cache, block_table, seq_lens)  # paged cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, scale=None, causal=False)   # gradients
@@ -20,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_varlen", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
+__all__ = ["fwd", "fwd_fp8", "fwd_varlen", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
            "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
@@ -32,13 +33,14 @@ FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp]),
     "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                            _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -176,6 +178,33 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
                           B, H, Nq, Nk, d, float(scale), _causal_arg(causal), _dtype_code(q),
                           _stream_ptr(q.device))
     _raise(st, "fa_fwd")
+    return out, lse
+
+
+def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
+            scale: float | None = None, causal=False, out=None, lse=None):
+    """Attention forward on E4M3 inputs (torch.float8_e4m3fn [B, H, N, 128] GPU tensors); the
+    real inputs are q * q_descale etc. Returns (o float32 [B, H, Nq, d], lse [B, H, Nq])."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] GPU tensor")
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError(f"{name} must be torch.float8_e4m3fn")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = library().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, H, Nq, Nk, d, float(scale), float(q_descale), float(k_descale),
+                              float(v_descale), _causal_arg(causal), _stream_ptr(q.device))
+    _raise(st, "fa_fwd_fp8")
     return out, lse
 
 

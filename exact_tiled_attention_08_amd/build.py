@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip",
+           "fa_fwd_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -139,6 +139,44 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, f
   return finish_launch(fa::launch_fwd_bf16_varlen(p, d, causal != 0, (hipStream_t)stream));
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, float scale, float q_descale,
+                     float k_descale, float v_descale, int causal, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX || BH * (long long)Nq * d > (1LL << 62) / 4) return FA_ERR_SHAPE;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
+  if (!(q_descale > 0.f) || !isfinite(q_descale) || !(k_descale > 0.f) || !isfinite(k_descale) ||
+      !(v_descale > 0.f) || !isfinite(v_descale))
+    return FA_ERR_VALUE;
+  const float c = scale * q_descale * k_descale * fa::kLog2e;
+  if (!isfinite(c) || !(c > 0.f)) return FA_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  const int br = fa::fwd_fp8_block_rows();
+  const long long nqt = (Nq + br - 1) / br;
+  if (BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)BH;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.off = query_offset(causal, Nq, Nk);
+  p.nqt = (int)nqt;
+  p.hpg = heads_per_group((int)BH, nqt);
+  p.c = c;
+  p.vscale = v_descale;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  return finish_launch(fa::launch_fwd_fp8(p, causal != 0, (hipStream_t)stream));
+}
+
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   if (B < 1 || H < 1 || d < 1 || num_splits < 1) return 0;
   const unsigned long long n = (unsigned long long)B * H * num_splits;

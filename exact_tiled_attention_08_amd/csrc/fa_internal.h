@@ -28,7 +28,8 @@ struct FwdParams {
   int off;        // key position of query row 0 for causal masking (Nk - Nq or 0)
   int nqt;        // number of query tiles per (b, h)
   int hpg;        // (b, h) pairs per XCD group for the block -> tile mapping
-  float c;        // scale * log2(e): scores are exponentiated base 2
+  float c;        // scale * log2(e): scores are exponentiated base 2 (FP8: times both descales)
+  float vscale;   // FP8 only: the descale factor of v
   // Packed variable-length batches only: q, k, v, o are [total][H][d], lse [H][total_q];
   // sequence b owns rows cu_q[b] .. cu_q[b+1]-1 (queries) and cu_k[b] .. cu_k[b+1]-1 (keys).
   const int* cu_q;
@@ -123,6 +124,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 // Launchers (defined next to their kernels). Each returns the hipError_t of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_bf16_varlen(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, hipStream_t s);
+int fwd_fp8_block_rows();
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s);

@@ -81,6 +81,23 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
                  fa_dtype dtype, void* stream);
 
 /*
+ * fa_fwd_fp8 — fa_fwd with 8-bit floating-point inputs on the FP8 matrix cores ("FlashAttention:
+ * Attention Is Limited by Memory, Not Math", section "FlashAttention 1, 2 and 3": FP8 is one
+ * of FlashAttention-3's additions).
+ *   q [B][H][Nq][d], k, v [B][H][Nk][d]: OCP E4M3 bytes (1 sign, 4 exponent bits with bias
+ *   7, 3 mantissa bits, no infinities); the real inputs are q * q_descale, k * k_descale,
+ *   v * v_descale (finite, > 0).
+ *   o [B][H][Nq][d] float32; lse [B][H][Nq] float32 or NULL.
+ *   d = 128; scale, causal and the empty-row policy as in fa_fwd.
+ * Scores are float32 (the q.k products and their sums are exact up to float32 rounding);
+ * the probabilities enter the second product as E4M3(256 * exp(s - m)), rounded to nearest
+ * even with the row's largest weight exact; the normaliser sums the float32 weights.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, float scale, float q_descale,
+                     float k_descale, float v_descale, int causal, void* stream);
+
+/*
  * fa_fwd_varlen — fa_fwd over a packed batch of variable-length sequences (no padding).
  *   q [total_q][H][d], k, v [total_k][H][d]  FA_BF16     o [total_q][H][d] float32
  *   lse [H][total_q] float32 or NULL

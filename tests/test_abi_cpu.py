@@ -214,3 +214,24 @@ def _varlen(**kw):
 ])
 def test_varlen_rejects(kw, status):
     assert _varlen(**kw) == status
+
+
+def _fp8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=100, Nk=90, d=128, scale=0.1, qd=0.01, kd=0.02,
+             vd=0.03, causal=1, stream=None)
+    a.update(kw)
+    return fa.library().fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                   a["Nk"], a["d"], a["scale"], a["qd"], a["kd"], a["vd"], a["causal"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(Nk=0), fa.FA_ERR_SHAPE),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(Nk=1 << 24), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(qd=0.0), fa.FA_ERR_VALUE), (dict(kd=-1.0), fa.FA_ERR_VALUE),
+    (dict(vd=float("inf")), fa.FA_ERR_VALUE), (dict(causal=5), fa.FA_ERR_VALUE),
+    (dict(q=P + 4), fa.FA_ERR_ALIGN), (dict(v=P + 8), fa.FA_ERR_ALIGN),
+])
+def test_fp8_rejects(kw, status):
+    assert _fp8(**kw) == status

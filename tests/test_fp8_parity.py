@@ -1,0 +1,127 @@
+"""GPU parity of the 8-bit prefill (fa_fwd_fp8) against the float64 oracle on the exactly
+dequantized inputs (E4M3 value * descale).
+
+Tolerance (derived from the arithmetic; the stated bounds cover bfloat16 and float32): the
+scores are float32 sums of exact products; each weight enters the second product as
+E4M3(256 p), whose relative rounding error is at most 2^-4 (three mantissa bits), while the
+normaliser sums the float32 weights. So every output element is off by at most
+2^-4 * sum_j p_j |v_j| <= 2^-4 * max|V| (plus float32 rounding; weights below 2^-18 of the
+row max, which E4M3 cannot hold, carry negligible mass). A float32 model of this arithmetic
+stays within 0.07 (max) and 0.004 (mean) on N = 512..4096 with and without the causal mask
+and with the sharp x3 inputs. Bounds:
+    max|O - O*| <= 2^-4 * max|V|,   mean|O - O*| <= 1e-2,   max|LSE - LSE*| <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_08_amd as fa
+import oracle
+import workloads as W
+from parity_util import rows_of, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+FP8_MEAN, FP8_LSE = 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.library()
+
+
+def _deq(x8, d):
+    return x8.cpu().to(torch.float64) * d
+
+
+def compare_fp8(o, lse, o_ref, l_ref, vmax, what):
+    o = np.asarray(o, np.float64).reshape(o_ref.shape)
+    lse = np.asarray(lse, np.float64).reshape(l_ref.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf LSE rows differ"
+    assert np.all(o[empty] == 0.0), f"{what}: empty rows must be zero"
+    err = np.abs(o - o_ref)
+    lerr = np.abs(lse[~empty] - l_ref[~empty]) if np.any(~empty) else np.zeros(1)
+    st = dict(o_max=float(err.max()), o_mean=float(err.mean()), lse_max=float(lerr.max()),
+              bound=2.0 ** -4 * vmax)
+    assert st["o_max"] <= st["bound"], f"{what}: O max err {st['o_max']:.3e} > {st['bound']:.3e}"
+    assert st["o_mean"] <= FP8_MEAN, f"{what}: O mean err {st['o_mean']:.3e}"
+    assert st["lse_max"] <= FP8_LSE, f"{what}: LSE max err {st['lse_max']:.3e}"
+    return st
+
+
+def _case(B, H, nq, nk, causal, seed, mult=2.0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    xs = [torch.randn((B, H, n, 128), generator=g, device=DEV) * m
+          for n, m in ((nq, mult), (nk, mult), (nk, 1.0))]
+    (q8, qd), (k8, kd), (v8, vd) = (W.quantize_e4m3(x) for x in xs)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    vdeq = _deq(v8, vd)
+    o_ref, l_ref = oracle.attention(_deq(q8, qd), _deq(k8, kd), vdeq, scale, causal)
+    return compare_fp8(o.cpu().numpy().reshape(-1, 128), lse.cpu().numpy().reshape(-1), o_ref, l_ref,
+                       float(vdeq.abs().max()), f"fp8 Nq={nq} Nk={nk} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [0, 1, 2], ids=["full", "causal", "topleft"])
+def test_fp8_edge_grid(causal):
+    pairs = [(1, 1), (17, 17), (63, 64), (127, 129), (128, 128), (255, 257), (256, 256), (300, 1000),
+             (1000, 300), (1, 700), (700, 1), (129, 128)]
+    worst = {}
+    for i, (nq, nk) in enumerate(pairs):
+        say(f"fp8 edge causal={causal} Nq={nq} Nk={nk}")
+        st = _case(2, 3, nq, nk, causal, 900 + i)
+        for key in ("o_max", "o_mean", "lse_max"):
+            worst[key] = max(worst.get(key, 0.0), st[key])
+    say(f"  worst {worst}")
+
+
+@pytest.mark.parametrize("num,per_head", [(3, 32), (4, 16)])
+def test_fp8_workload_sampled(num, per_head):
+    """The causal N = 8192 (sharp x3) and N = 30000 workloads in E4M3 at full size, sampled
+    rows compared with the oracle over all their keys."""
+    w = W.WORKLOADS[num]
+    say(f"fp8 workload {num}: {w.name}")
+    (q8, qd), (k8, kd), (v8, vd) = W.make_inputs_fp8(w, DEV)
+    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(w, per_head)
+    vdeq = _deq(v8, vd)
+    o_ref, l_ref = oracle.attention(_deq(q8, qd), _deq(k8, kd), vdeq, w.scale, w.causal, rows=rows)
+    st = compare_fp8(rows_of(o, rows, w.d), rows_of(lse, rows), o_ref, l_ref, float(vdeq.abs().max()),
+                     w.name)
+    say(f"  {st}")
+
+
+def test_fp8_constant_values_and_determinism():
+    """V = 1: O = sum(P~) / l, within 2^-4 of 1; two calls agree bit for bit."""
+    g = torch.Generator(device=DEV).manual_seed(77)
+    q8, qd = W.quantize_e4m3(torch.randn((2, 2, 500, 128), generator=g, device=DEV) * 2)
+    k8, kd = W.quantize_e4m3(torch.randn((2, 2, 500, 128), generator=g, device=DEV) * 2)
+    ones = torch.ones((2, 2, 500, 128), device=DEV).to(torch.float8_e4m3fn)
+    say("fp8 V = 1")
+    o, _ = fa.fwd_fp8(q8, k8, ones, qd, kd, 1.0, causal=1)
+    torch.cuda.synchronize()
+    assert float((o - 1.0).abs().max()) <= 2.0 ** -4
+    a = fa.fwd_fp8(q8, k8, ones, qd, kd, 1.0, causal=0)
+    b = fa.fwd_fp8(q8, k8, ones, qd, kd, 1.0, causal=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_fp8_python_layer_rejects_on_gpu():
+    x = torch.zeros((1, 1, 4, 128), device=DEV).to(torch.float8_e4m3fn)
+    with pytest.raises(ValueError):
+        fa.fwd_fp8(x.to(torch.bfloat16), x, x, 1.0, 1.0, 1.0)
+    with pytest.raises(ValueError):
+        fa.fwd_fp8(x, x, x, 1.0, 0.0, 1.0)          # descale must be > 0
+    y = torch.zeros((1, 1, 4, 64), device=DEV).to(torch.float8_e4m3fn)
+    with pytest.raises(NotImplementedError):
+        fa.fwd_fp8(y, y, y, 1.0, 1.0, 1.0)           # d = 128 only

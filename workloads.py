@@ -105,6 +105,29 @@ def make_inputs(w: Workload, device="cpu"):
     return q, k, v
 
 
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor E4M3 quantisation: descale = max|x| / 448 (the largest finite E4M3 value),
+    x8 = E4M3(x / descale) rounded to nearest even. Returns (x8, descale); the value the
+    kernel and the oracle both use is x8 * descale. Data preparation only."""
+    amax = float(x.abs().max())
+    descale = amax / 448.0 if amax > 0 else 1.0
+    descale = float(torch.tensor(descale, dtype=torch.float32))  # the kernel takes float32
+    x8 = (x.float() / descale).to(torch.float8_e4m3fn)
+    return x8, descale
+
+
+def make_inputs_fp8(w: Workload, device="cpu"):
+    """E4M3 versions of workload w's Q, K, V: the recipe's float32 draws (same seeds and
+    factors) quantised per tensor with quantize_e4m3. Returns ((q8, qd), (k8, kd), (v8, vd))."""
+    c = w.number
+    out = []
+    for t, (n, mult) in enumerate(((w.Nq, w.qk_mult), (w.Nk, w.qk_mult), (w.Nk, 1.0))):
+        x = draw((w.B, w.H, n, w.d), 10 * c + t, mult, torch.float32, device)
+        out.append(quantize_e4m3(x))
+        del x
+    return tuple(out)
+
+
 def make_grad(w: Workload, device="cpu"):
     """dO, the gradient fed to the backward pass: N(0,1) of q's shape and dtype, seed 10c + 3."""
     return draw((w.B, w.H, w.Nq, w.d), 10 * w.number + 3, 1.0, w.dtype, device)
