@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   // (P = exp2(S c - LSE2), dS = P (dP - D), rounding to bfloat16) is spread over group 1's
   // MFMAs and that of step 1 over group 2's, so the matrix core and the vector ALU of the
   // SIMD work at the same time.
-  auto plain_tile = [&](const char* Qs, const char* dOs, const float* sts, const f32x16 (&sinit)[2]) {
+  auto tile_stream = [&](const char* Qs, const char* dOs, const float* sts, const f32x16 (&sinit)[2]) {
     constexpr int NG = D / 8, NF = 4 * NG, RING = 6, EPM = 16 / NG;  // elements per MFMA
     f32x16 s[2], dp[2];
     bf16x8 pb[2][2], dsb[2][2];
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) sinit[x][e] = (8 * (e >> 2) + (e & 3) < lim) ? -INFINITY : 0.f;
       }
     }
-    plain_tile(Qs, dOs, sts, sinit);
+    tile_stream(Qs, dOs, sts, sinit);
   }
 
   // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4.
