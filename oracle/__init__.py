@@ -6,7 +6,8 @@ links or calls it, and it imports nothing from the HIP library: the two share
 only the seeded input generators in ``workloads.py``.
 
 ``attention`` evaluates the plain definition O = softmax(Q K^T * scale + mask) V
-row by row in double precision (the C source states each passage it follows);
+row by row in double precision (the C source states each passage it follows), with an
+optional additive bias on the scaled scores;
 ``attention_bwd`` evaluates the gradients of sum(O * dO) with respect to Q, K, V
 from the same definition by the chain rule. ``paged_attention`` is the same definition
 for one query per sequence whose keys and values live in a paged cache: it first
@@ -53,6 +54,15 @@ def load_library(path: str):
                   ctypes.c_double, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    fb = lib.oracle_attention_bias
+    fb.restype = ctypes.c_int
+    fb.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong,
+                   ctypes.c_longlong,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_double, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     g = lib.oracle_attention_bwd
     g.restype = ctypes.c_int
     g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -115,8 +125,27 @@ def _causal_code(causal) -> int:
     return c
 
 
+def _bias_view(bias, B: int, H: int, Nq: int, Nk: int):
+    """(tensor kept alive, dtype code, (sb, sh, sq)) for a CPU bias tensor broadcastable
+    to [B, H, Nq, Nk]: element (b, h, i, j) is at b*sb + h*sh + i*sq + j of the tensor's
+    data (a broadcast dimension gets stride 0)."""
+    import torch
+    bt = torch.as_tensor(bias).detach().cpu()
+    if bt.dtype not in (torch.bfloat16, torch.float32, torch.float64):
+        raise TypeError(f"bias must be bfloat16, float32 or float64, got {bt.dtype}")
+    while bt.dim() < 4:
+        bt = bt.unsqueeze(0)
+    if bt.dim() != 4:
+        raise ValueError("bias must broadcast to [B, H, Nq, Nk]")
+    if bt.shape[3] != Nk or bt.stride(3) != 1:   # keys must be contiguous: spell them out
+        bt = bt.expand(*bt.shape[:3], Nk).contiguous()
+    be = bt.expand(B, H, Nq, Nk)                  # raises if not broadcastable
+    code = {torch.bfloat16: BF16, torch.float32: F32, torch.float64: F64}[bt.dtype]
+    return be, code, tuple(int(x) for x in be.stride()[:3])
+
+
 def attention(q, k, v, scale: float, causal: bool = False, rows=None,
-              want_p: bool = False, threads: int | None = None):
+              want_p: bool = False, threads: int | None = None, bias=None):
     """Float64 attention for q [B,H,Nq,d], k/v [B,H,Nk,d] (float32, bfloat16 or float64;
     float64 carries exactly dequantized 8-bit inputs).
 
@@ -126,6 +155,8 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
     ``rows``: optional flat row ids (b*H + h)*Nq + i to evaluate (sampled
     checks); default all rows. ``scale`` is used as the exact double given;
     callers pass the float32-rounded value the kernel receives.
+    ``bias``: optional CPU tensor (bfloat16, float32 or float64) broadcastable to
+    [B, H, Nq, Nk], added to the scaled scores of visible pairs (-inf hides a key).
     Returns (o [nrows, d] float64, lse [nrows] float64[, p [nrows, Nk]]).
     """
     qa, dt = _as_input(q)
@@ -150,12 +181,18 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
     lse = np.empty((nrows,), np.float64)
     p = np.empty((nrows, Nk), np.float64) if want_p else None
     scratch = np.empty((threads, Nk), np.float64)
-    rc = _load().oracle_attention(
-        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, B, H, Nq, Nk, d,
-        float(scale), _causal_code(causal),
-        rows_arr.ctypes.data if rows_arr is not None else None, nrows, threads,
-        scratch.ctypes.data, o.ctypes.data, lse.ctypes.data,
-        p.ctypes.data if p is not None else None)
+    tail = (float(scale), _causal_code(causal),
+            rows_arr.ctypes.data if rows_arr is not None else None, nrows, threads,
+            scratch.ctypes.data, o.ctypes.data, lse.ctypes.data,
+            p.ctypes.data if p is not None else None)
+    if bias is None:
+        rc = _load().oracle_attention(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
+                                      B, H, Nq, Nk, d, *tail)
+    else:
+        bt, bcode, (sb, sh, sq) = _bias_view(bias, B, H, Nq, Nk)
+        rc = _load().oracle_attention_bias(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
+                                           bt.data_ptr(), bcode, sb, sh, sq,
+                                           B, H, Nq, Nk, d, *tail)
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
     return (o, lse, p) if want_p else (o, lse)

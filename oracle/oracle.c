@@ -32,6 +32,14 @@
  *   - A row with no visible key returns O = 0: same page and section (the
  *     explicit empty-row policy). Its log-sum-exp is -inf (the log of an
  *     empty sum).
+ *   - An additive bias (optional, oracle_attention_bias) is added to the
+ *     scaled score of every visible pair before the softmax: same page,
+ *     section "Keep only the state needed for the final weighted average"
+ *     (scores are scaled, then the intended mask or bias is added). Reading
+ *     taken where the pages are silent: the bias is not multiplied by the
+ *     scale, a key hidden by the causal mask stays hidden whatever its bias,
+ *     and a bias of -inf hides a key like the mask does (so a row whose keys
+ *     all carry -inf is an empty row).
  *   - The per-row statistic saved for a backward pass is reported as
  *     LSE = m + ln(l), in natural-log units of the scaled, masked scores:
  *     "Flash Attention Optimization", section "Sizing a tile, and why the
@@ -67,6 +75,15 @@ static long long query_offset(int causal, int Nq, int Nk) {
   return causal == 2 ? 0 : (long long)Nk - (long long)Nq;
 }
 
+/* Optional additive bias: element (b, h, i, j) sits at index
+ * b*sb + h*sh + i*sq + j of p (a stride of 0 repeats the same values along that
+ * dimension). p == NULL means no bias. */
+typedef struct {
+  const void* p;
+  int dtype;
+  long long sb, sh, sq;
+} bias_view;
+
 /*
  * One query row: row id r = (b*H + h)*Nq + i.
  * s   : scratch of Nk doubles (scores, then unnormalised weights)
@@ -74,13 +91,16 @@ static long long query_offset(int causal, int Nq, int Nk) {
  */
 static void one_row(const void* q, const void* k, const void* v, int dtype,
                     int H, int Nq, int Nk, int d, double scale, int causal,
+                    const bias_view* bias,
                     long long r, double* s, double* o, double* lse, double* p) {
   long long bh = r / Nq;
   int i = (int)(r % Nq);
   size_t qoff = (size_t)r * (size_t)d;
   size_t kvbase = (size_t)bh * (size_t)Nk * (size_t)d;
   long long last_visible = causal ? (long long)i + query_offset(causal, Nq, Nk) : (long long)Nk - 1;
-  (void)H;
+  size_t brow = 0; /* index of bias element (b, h, i, 0) */
+  if (bias && bias->p)
+    brow = (size_t)((bh / H) * bias->sb + (bh % H) * bias->sh + (long long)i * bias->sq);
 
   /* scores of visible keys; masked keys are -inf */
   double m = -INFINITY;
@@ -90,6 +110,7 @@ static void one_row(const void* q, const void* k, const void* v, int dtype,
     for (int t = 0; t < d; ++t)
       dot += widen(q, dtype, qoff + t) * widen(k, dtype, kvbase + (size_t)j * d + t);
     s[j] = scale * dot;
+    if (bias && bias->p) s[j] += widen(bias->p, bias->dtype, brow + (size_t)j);
     if (s[j] > m) m = s[j];
   }
 
@@ -116,26 +137,20 @@ static void one_row(const void* q, const void* k, const void* v, int dtype,
   if (p) for (int j = 0; j < Nk; ++j) p[j] = s[j] / l;
 }
 
-/*
- * oracle_attention
- *   q [B][H][Nq][d], k and v [B][H][Nk][d], contiguous, dtype ORACLE_F32 or
- *   ORACLE_BF16 (raw bfloat16 bit patterns).
- *   rows   : list of nrows flat row ids (b*H + h)*Nq + i, or NULL for all
- *            B*H*Nq rows in order.
- *   o      : [nrows][d] doubles;  lse : [nrows] doubles;
- *   p      : [nrows][Nk] doubles or NULL (the probability rows, small cases).
- *   scratch: caller-owned, nthreads_max * Nk doubles (one score row per
- *            thread); nthreads_max is the value the caller passes as nthreads.
- * Returns 0, or -1 for an invalid argument.
- */
-int oracle_attention(const void* q, const void* k, const void* v, int dtype,
-                     int B, int H, int Nq, int Nk, int d, double scale, int causal,
-                     const long long* rows, long long nrows, int nthreads,
-                     double* scratch, double* o, double* lse, double* p) {
+/* Shared checks and row loop of oracle_attention and oracle_attention_bias. */
+static int attention_rows(const void* q, const void* k, const void* v, int dtype,
+                          int B, int H, int Nq, int Nk, int d, double scale, int causal,
+                          const bias_view* bias,
+                          const long long* rows, long long nrows, int nthreads,
+                          double* scratch, double* o, double* lse, double* p) {
   if (!q || !k || !v || !o || !lse || !scratch) return -1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
   if (causal < 0 || causal > 2) return -1;
+  if (bias && bias->p) {
+    if (bias->dtype != ORACLE_F32 && bias->dtype != ORACLE_BF16 && bias->dtype != ORACLE_F64) return -1;
+    if (bias->sb < 0 || bias->sh < 0 || bias->sq < 0) return -1;
+  }
   long long total = (long long)B * H * Nq;
   if (!rows) nrows = total;
   for (long long n = 0; rows && n < nrows; ++n)
@@ -149,11 +164,47 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
     tid = omp_get_thread_num();
 #endif
     long long r = rows ? rows[n] : n;
-    one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, r,
+    one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, bias, r,
             scratch + (size_t)tid * (size_t)Nk, o + (size_t)n * d, lse + n,
             p ? p + (size_t)n * Nk : NULL);
   }
   return 0;
+}
+
+/*
+ * oracle_attention
+ *   q [B][H][Nq][d], k and v [B][H][Nk][d], contiguous, dtype ORACLE_F32,
+ *   ORACLE_BF16 (raw bfloat16 bit patterns) or ORACLE_F64.
+ *   rows   : list of nrows flat row ids (b*H + h)*Nq + i, or NULL for all
+ *            B*H*Nq rows in order.
+ *   o      : [nrows][d] doubles;  lse : [nrows] doubles;
+ *   p      : [nrows][Nk] doubles or NULL (the probability rows, small cases).
+ *   scratch: caller-owned, nthreads_max * Nk doubles (one score row per
+ *            thread); nthreads_max is the value the caller passes as nthreads.
+ * Returns 0, or -1 for an invalid argument.
+ */
+int oracle_attention(const void* q, const void* k, const void* v, int dtype,
+                     int B, int H, int Nq, int Nk, int d, double scale, int causal,
+                     const long long* rows, long long nrows, int nthreads,
+                     double* scratch, double* o, double* lse, double* p) {
+  return attention_rows(q, k, v, dtype, B, H, Nq, Nk, d, scale, causal, NULL,
+                        rows, nrows, nthreads, scratch, o, lse, p);
+}
+
+/*
+ * oracle_attention_bias: as oracle_attention, with the additive bias
+ *   S[b][h][i][j] = scale * q_i . k_j + bias[b*sb + h*sh + i*sq + j]
+ * (bias of dtype bdtype, strides in elements, each >= 0; 0 repeats a dimension).
+ */
+int oracle_attention_bias(const void* q, const void* k, const void* v, int dtype,
+                          const void* bias, int bdtype, long long sb, long long sh, long long sq,
+                          int B, int H, int Nq, int Nk, int d, double scale, int causal,
+                          const long long* rows, long long nrows, int nthreads,
+                          double* scratch, double* o, double* lse, double* p) {
+  if (!bias) return -1;
+  bias_view bv = {bias, bdtype, sb, sh, sq};
+  return attention_rows(q, k, v, dtype, B, H, Nq, Nk, d, scale, causal, &bv,
+                        rows, nrows, nthreads, scratch, o, lse, p);
 }
 
 /*
@@ -185,7 +236,7 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
 static void row_stats(const void* q, const void* k, const void* v, const void* dout,
                       int dtype, int H, int Nq, int Nk, int d, double scale, int causal,
                       long long r, double* s, double* o, double* lse, double* dsum) {
-  one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, r, s, o, lse, NULL);
+  one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, NULL, r, s, o, lse, NULL);
   double acc = 0.0;
   for (int t = 0; t < d; ++t) acc += widen(dout, dtype, (size_t)r * d + t) * o[t];
   *dsum = acc;
