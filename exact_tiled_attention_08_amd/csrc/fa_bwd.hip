@@ -380,8 +380,15 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
     }
   }
   // padding rows (qrow >= Nq, < Nq_pad) carry LSE2 = +inf: their probabilities are 0
-  const float lse2 = wsh[stat_index(qrow)];
-  const float dsum = wsh[stat_index(qrow) + 64];
+  float lse2 = wsh[stat_index(qrow)];
+  float dsum = wsh[stat_index(qrow) + 64];
+  // Pass the row data through an empty asm before the first tile load: the compiler then
+  // waits for these loads once, here, instead of waiting inside the loop with a count
+  // that ignores the in-flight tile loads (which would hold each step until the next
+  // tile had landed).
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]), "+v"(df[kk]));
+  asm volatile("" : "+v"(lse2), "+v"(dsum));
 
   int kv_end = p.Nk;
   int wave_kv_end = (wq0 < p.Nq) ? p.Nk : 0;

@@ -257,6 +257,11 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
   f32x16 s[NKB];
   if (ntiles > 0) issue(0, loader ? kbuf(0) : vbuf(0));
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 have landed
+  // Q through an empty asm: otherwise a merged path that bypasses the wait above makes the
+  // compiler wait for the Q loads (vmcnt(0), which includes the tile loads just issued)
+  // inside every matrix phase.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qb[kk]));
   if (ntiles > 0) {
     wg_barrier();
     if (ntiles > 1) issue(1, loader ? kbuf(1) : vbuf(1));
