@@ -130,6 +130,43 @@ def prefill_record(num: int, steps: int, warmup: int):
     return rec, (w, q, k, v)
 
 
+def bias_record(num: int, steps: int, warmup: int):
+    """fa_fwd_bias on workload `num` with a full [B, H, Nq, Nk] bias of its dtype (seeded,
+    N(0,1) x 2): the general additive bias, nothing broadcast."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[num]
+    q, k, v = W.make_inputs(w, "cuda")
+    bias = W.make_bias(w, "cuda")
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fwd_bias(q, k, v, bias, scale=w.scale, causal=w.causal, out=o, lse=lse)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    # bias elements of the visible (query, key) pairs: each is read once; with Q, K, V, O
+    # and LSE that puts the launch below the ridge (HBM-bound) for a full bias
+    pairs = w.Nq * (w.Nq + 1) // 2 if w.causal and w.Nq == w.Nk else w.Nq * w.Nk
+    bias_bytes = w.B * w.H * pairs * bias.element_size()
+    nbytes = w.io_bytes + bias_bytes
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    rec = {
+        "workload": f"{w.name}, plus a full [B, H, Nq, Nk] bias",
+        "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+        "flops_per_launch": w.flops, "bias_bytes_per_launch": bias_bytes,
+        "bytes_per_launch": nbytes, "flop_per_byte": w.flops / nbytes,
+        "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+    }
+    del q, k, v, bias, o, lse
+    torch.cuda.empty_cache()
+    return rec
+
+
 def fp8_record(num: int, steps: int, warmup: int):
     """fa_fwd_fp8 on workload `num`'s shape with its draws quantised per tensor to E4M3."""
     import torch
@@ -312,7 +349,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the N=30000 and decode legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen", "fp8"],
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen", "fp8",
+                                       "bias"],
                     default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
@@ -336,6 +374,9 @@ def main():
         return
     if args.only == "fp8":
         print(json.dumps({"prefill_fp8": fp8_record(args.workload, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "bias":
+        print(json.dumps({"prefill_bias": bias_record(args.workload, args.steps, args.warmup)}), flush=True)
         return
     if args.only == "varlen":
         print(json.dumps({"prefill_varlen": varlen_record(args.steps, args.warmup)}), flush=True)
@@ -380,6 +421,7 @@ def main():
         torch.cuda.empty_cache()
         extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["prefill_fp8_N30000"] = fp8_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
+        extra["prefill_bias"] = bias_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["prefill_varlen"] = varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
         extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))

@@ -6,6 +6,7 @@ There is no CPU or PyTorch fallback: if the library is missing, or a tensor is
 not on the GPU, the call raises.
 
     o, lse = fwd(q, k, v, scale=None, causal=False)        # prefill
+    o, lse = fwd_bias(q, k, v, bias, scale=None, causal=False)   # plus an additive bias
     o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)  # packed batch
     o, lse = fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale)   # E4M3 inputs
     o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
@@ -21,7 +22,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_fp8", "fwd_varlen", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
+__all__ = ["fwd", "fwd_bias", "pad_bias", "fwd_fp8", "fwd_varlen", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
            "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
@@ -33,13 +34,15 @@ FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
+EXPORTS = ("fa_fwd", "fa_fwd_bias", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
+    "fa_fwd_bias": (_i, [_vp, _vp, _vp, _vp, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+                         _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp]),
     "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                            _vp]),
@@ -178,6 +181,72 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
                           B, H, Nq, Nk, d, float(scale), _causal_arg(causal), _dtype_code(q),
                           _stream_ptr(q.device))
     _raise(st, "fa_fwd")
+    return out, lse
+
+
+def pad_bias(bias):
+    """A view of `bias` (any shape, keys last) whose key dimension sits in rows padded to a
+    multiple of 8 elements, as fwd_bias needs for bfloat16; a copy into a new buffer."""
+    import torch
+    nk = bias.shape[-1]
+    buf = torch.zeros((*bias.shape[:-1], -(-nk // 8) * 8), dtype=bias.dtype, device=bias.device)
+    buf[..., :nk].copy_(bias)
+    return buf[..., :nk]
+
+
+def _bias_strides(bias, q, B: int, H: int, Nq: int, Nk: int):
+    """Element strides (b, h, q) of a bias broadcast to [B, H, Nq, Nk], after checking what
+    the kernels read: keys contiguous, and for bfloat16 each row readable up to its first Nk
+    elements rounded up to a multiple of 8."""
+    import torch
+    if not isinstance(bias, torch.Tensor) or not bias.is_cuda or bias.device != q.device:
+        raise ValueError("bias must be a GPU tensor on q's device")
+    if bias.dtype != q.dtype:
+        raise ValueError(f"bias must have q's dtype {q.dtype}, got {bias.dtype}")
+    if bias.dim() > 4:
+        raise ValueError("bias must broadcast to [B, H, Nq, Nk]")
+    bt = bias.reshape((1,) * (4 - bias.dim()) + tuple(bias.shape)) if bias.dim() < 4 else bias
+    if bt.shape[3] != Nk or (Nk > 1 and bt.stride(3) != 1):
+        raise ValueError("the bias key dimension must have size Nk and stride 1")
+    try:
+        be = bt.expand(B, H, Nq, Nk)
+    except RuntimeError as e:
+        raise ValueError(f"bias of shape {tuple(bias.shape)} does not broadcast to "
+                         f"[{B}, {H}, {Nq}, {Nk}]") from e
+    sb, sh, sq = (int(x) for x in be.stride()[:3])
+    if q.dtype == torch.bfloat16:
+        last = bt.storage_offset() + (B - 1) * sb + (H - 1) * sh + (Nq - 1) * sq + -(-Nk // 8) * 8
+        if (sb | sh | sq) % 8 or be.data_ptr() % 16 or last * 2 > bt.untyped_storage().nbytes():
+            raise ValueError("a bfloat16 bias needs 16-byte aligned rows whose key dimension is "
+                             "padded to a multiple of 8 elements: pass pad_bias(bias)")
+    return be, sb, sh, sq
+
+
+def fwd_bias(q, k, v, bias, scale: float | None = None, causal: bool = False, out=None, lse=None,
+             return_lse: bool = True):
+    """Attention forward with an additive bias on the scaled scores (q's dtype, broadcastable
+    to [B, H, Nq, Nk], keys contiguous; -inf hides a key). Returns (o, lse)."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    be, sb, sh, sq = _bias_strides(bias, q, B, H, Nq, Nk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    elif out.shape != (B, H, Nq, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, H, Nq, d] tensor")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32
+                              or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    st = library().fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), be.data_ptr(), sb, sh, sq,
+                               out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                               B, H, Nq, Nk, d, float(scale), _causal_arg(causal), _dtype_code(q),
+                               _stream_ptr(q.device))
+    _raise(st, "fa_fwd_bias")
     return out, lse
 
 

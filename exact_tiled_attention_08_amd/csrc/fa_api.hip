@@ -49,7 +49,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     case FA_ERR_VALUE: return "scale must be finite and > 0; causal must be 0, 1 or 2";
-    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_ALIGN: return "a tensor pointer (or a bias stride) is not suitably aligned";
   }
   return "unknown status";
 }
@@ -91,6 +91,61 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, d, causal != 0, (hipStream_t)stream)
                                   : fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream);
+  return finish_launch(e);
+}
+
+fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      float* o, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                      int causal, fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !bias) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX || BH * (long long)Nq * d > (1LL << 62) / 4) return FA_ERR_SHAPE;
+  if (bias_stride_b < 0 || bias_stride_h < 0 || bias_stride_q < 0) return FA_ERR_SHAPE;
+  // 64-bit element offsets of the farthest bias row stay far from overflow
+  const long long lim = (1LL << 62) / 4;
+  if (bias_stride_b > lim / B || bias_stride_h > lim / H || bias_stride_q > lim / Nq)
+    return FA_ERR_SHAPE;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
+  // the bias of one wave's 32 query rows is addressed with 32-bit byte offsets
+  if (bias_stride_q * 64 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (dtype == FA_BF16) {
+    if (!aligned16(bias) || (bias_stride_b | bias_stride_h | bias_stride_q) % 8 != 0)
+      return FA_ERR_ALIGN;
+  } else if (((uintptr_t)bias & 3u) != 0) {
+    return FA_ERR_ALIGN;
+  }
+
+  const int br = dtype == FA_BF16 ? fa::fwd_bf16_block_rows(d) : fa::fwd_f32_block_rows(d);
+  const long long nqt = (Nq + br - 1) / br;
+  if (BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)BH;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.off = query_offset(causal, Nq, Nk);
+  p.nqt = (int)nqt;
+  p.hpg = heads_per_group((int)BH, nqt);
+  p.c = scale * fa::kLog2e;
+  p.H = H;
+  p.bias = bias;
+  p.bsb = bias_stride_b;
+  p.bsh = bias_stride_h;
+  p.bsq = bias_stride_q;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16_bias(p, d, causal != 0, (hipStream_t)stream)
+                                  : fa::launch_fwd_f32_bias(p, d, causal != 0, (hipStream_t)stream);
   return finish_launch(e);
 }
 

@@ -41,6 +41,17 @@
 // a row stride of H*d elements (masks use positions inside the sequence). Its (b, h) pairs
 // are numbered head-major so that every XCD gets a share of every sequence.
 //
+// Additive bias (BIAS): the bias is added to the scaled scores before the softmax
+// ("Explain FlashAttention ...", section "Keep only the state needed for the final
+// weighted average": scaled scores plus the intended mask or bias). Each wave streams the
+// bias of its own 32 query rows for a tile (32 x 64 bfloat16, 4 KB) from global memory
+// straight into its own double-buffered LDS area, issuing tile j+2 while it folds in tile
+// j+1, and waits for exactly the loads it needs (loads complete in issue order), so the
+// K/V stream is never held up behind the bias. Rows are stored with the 16-byte chunk
+// index XORed with (row / 2) % 8, which leaves at most two lanes of a half-wave on one
+// bank pair when each lane reads its row's 4 keys. In log2 units the score becomes
+// s * scale * log2(e) + bias * log2(e); masked keys stay -inf whatever their bias.
+//
 // Rescaling: the offset is always the exact running max, so the largest weight of a row
 // is exactly 1 and survives the rounding of P to bfloat16 without error (an offset that
 // lags the max would leave the dominant weight at 2^delta, rounded by up to 2^-9 of its
@@ -101,10 +112,23 @@ __device__ __forceinline__ float wave_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, bool CAUSAL, bool VARLEN>
+// Bias staging of the BIAS kernel: per wave and buffer, 32 rows x BC keys of bfloat16.
+template <int BC>
+struct BiasCfg {
+  static constexpr int ROWB = BC * 2;           // bytes per row
+  static constexpr int WAVEB = 32 * ROWB;       // bytes per wave and buffer
+  static constexpr int LDS = 2 * kNW * WAVEB;   // two buffers for every wave
+  static constexpr int LOADS = WAVEB / (64 * 16);  // direct loads per lane per tile
+  static_assert(BC == 64, "the bias swizzle assumes 8 chunks of 16 bytes per row");
+};
+
+template <int D, int BC, bool CAUSAL, bool VARLEN, bool BIAS>
 __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D, BC>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  static_assert(!(BIAS && VARLEN), "bias is offered for dense batches only");
+  using BCfg = BiasCfg<BIAS ? BC : 64>;
+  constexpr int BIASLDS = BIAS ? BCfg::LDS : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS + BIASLDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,6 +178,17 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   }
   const int rs = VARLEN ? p.H * D : D;  // elements between consecutive rows
 
+  // Bias rows of this wave: element (row wq0 + r, key j) at bw + dr*bsq + j, where the
+  // row is clamped to Nq-1 (rows past Nq are computed but never stored) and dr = the
+  // clamped row minus bias_r0.
+  const uint16_t* bw = nullptr;
+  const int bias_r0 = min(wq0, Nq - 1);
+  if constexpr (BIAS) {
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    bw = (const uint16_t*)p.bias + (size_t)b * p.bsb + (size_t)h * p.bsh + (size_t)bias_r0 * p.bsq;
+  }
+
   // Q tile stays in VGPRs for the whole key loop, as the B operand of S^T = K Q^T.
   bf16x8 qb[D / 16];
 #pragma unroll
@@ -201,6 +236,44 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int n = 0; n < C::LOADS; ++n) dma(t, dst, n);
   };
+  // Bias of key tile t into this wave's buffer t % 2. Direct load n of lane L fills LDS
+  // slot 64n + L: row 8n + L/8, chunk position L%8, which holds the row's chunk
+  // position ^ ((row / 2) % 8). A chunk that starts at or past Nk is replaced by the
+  // chunk holding key Nk-1 (its keys are masked anyway), so the reads stay inside each
+  // row's first Nk elements rounded up to a multiple of 8.
+  char* const bias_lds = smem + C::LDS;
+  auto bias_buf = [&](int t) { return bias_lds + ((t & 1) * kNW + w) * BCfg::WAVEB; };
+  auto bias_issue = [&](int t) {
+    const int kv0 = t * BC;
+    const int cmax = (Nk - 1 - kv0) >> 3;
+    const char* base = (const char*)(bw + kv0);
+    char* dst = bias_buf(t);
+#pragma unroll
+    for (int n = 0; n < BCfg::LOADS; ++n) {
+      const int row = 8 * n + (lane >> 3);
+      const int dr = min(wq0 + row, Nq - 1) - bias_r0;
+      const int ch = min((lane & 7) ^ (((n & 1) << 2) | (lane >> 4)), cmax);
+      const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + n * 64 * 16));
+      dma16(base, (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)ch, lds);
+    }
+  };
+  // s <- s * scale * log2(e) + bias * log2(e) for tile t (this lane's query row, its 16
+  // keys per 32-key block: 32kb + 8(i/4) + 4g + i%4, one 8-byte read per 4 keys).
+  auto add_bias = [&](int t, f32x16 (&s)[BC / 32]) {
+    const char* row = bias_buf(t) + col * BCfg::ROWB;
+    const int sw = (col >> 1) & 7;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const v4i16 raw = *(const v4i16*)(row + (((4 * kb + qd) ^ sw) << 4) + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float bv = __uint_as_float((uint32_t)(uint16_t)raw[e] << 16);
+          s[kb][4 * qd + e] = __builtin_fmaf(s[kb][4 * qd + e], p.c, bv * kLog2e);
+        }
+      }
+  };
 
   // K fragment (A operand of S^T = K_j Q_i^T, BC keys x 32 queries per wave) of key block
   // kb and 16-dim contraction step kk.
@@ -231,14 +304,16 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   float l = 0.f;        // running sum over this lane's half of the keys
 
   // Online softmax of one tile; O is rescaled here, after the previous tile's PV and
-  // before this tile's, and only when some row of the wave raised its max.
+  // before this tile's, and only when some row of the wave raised its max. With a bias
+  // the scores arrive already in log2 units.
+  const float cs = BIAS ? 1.f : p.c;
   auto softmax = [&](f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    const float mt = wave_half_max(mx) * p.c;  // tile row max, log2 units (-inf if masked)
+    const float mt = wave_half_max(mx) * cs;  // tile row max, log2 units (-inf if masked)
     const bool raise = mt > m;
     const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.f;  // 0 when m was -inf
     m = raise ? mt : m;
@@ -248,7 +323,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], p.c, -m_use));
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], cs, -m_use));
         lsum += e;
         pb[2 * kb + (i >> 3)][i & 7] = (__bf16)e;  // round to nearest even
       }
@@ -319,15 +394,26 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   bf16x8 pb[BC / 16];
   f32x16 s[BC / 32];
   if (ntiles > 0) issue(0, loader ? kbuf(0) : vbuf(0));
+  if constexpr (BIAS)
+    if (ntiles > 0) bias_issue(0);
   // Q and tile 0 have landed. Waiting on every path with the builtin lets the compiler see
   // that the Q loads are complete, so it does not re-wait for them inside the loop (where
   // the wait would also stall on the in-flight tile loads that share the counter).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unchanged
+  // The compiler merges control flow so that some path into the loop bypasses that wait;
+  // it would then wait for the Q loads again before the first S^T MFMA of every matrix
+  // phase, and that vmcnt(0) would also stall on the tile loads just issued. Passing Q
+  // through an empty asm makes the loop's Q registers values that no load is pending on.
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qb[kk]));
   if (ntiles > 0) {
     wg_barrier();
     if (ntiles > 1) issue(1, loader ? kbuf(1) : vbuf(1));
+    if constexpr (BIAS)
+      if (ntiles > 1) bias_issue(1);
     if (wave_kv_end > 0) {
       compute_s(kbuf(0), s);
+      if constexpr (BIAS) add_bias(0, s);
       if (needs_mask(0)) mask_s(0, s);
       softmax(s, pb);
     }
@@ -344,15 +430,38 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // finished reading before that interval, and each group waits for its loads at the last
   // barrier before the first reader: group 0 before its step j+1 matrix phase, group 1
   // before its mid-step barrier of step j+1.
+  //
+  // With a bias, every wave also loads bias tile j+2 at the start of its vector phase of
+  // step j, and reads bias tile j+1 (loaded one step earlier) in that phase. Group 0's
+  // loads then run K_{j+1}, B_{j+1}, K_{j+2}, B_{j+2}, ...: at the start of step j it
+  // waits for all but the last bias batch (that is, for K_{j+1}), and before reading
+  // B_{j+1} for all but K_{j+2} and B_{j+2}. Group 1's wait for V_{j+1} also covers
+  // B_{j+1}, issued before it.
   auto step = [&](int j, int cur) {  // cur = j & 1, passed as a constant by the unrolled loop
-    if (loader) wait_loads();  // K_{j+1}
+    if (loader) {  // K_{j+1}
+      if constexpr (BIAS)
+        wait_loads_but<BCfg::LOADS>();
+      else
+        wait_loads();
+    }
     wg_barrier();
     if (loader && j + 2 < ntiles) issue(j + 2, kbuf(cur));
     const bool active = j * BC < wave_kv_end;
     if (active) matrix.template operator()<true>(vbuf(cur), kbuf(cur ^ 1), pb, s);
-    if (!loader) wait_loads();  // V_{j+1}
+    if (!loader) wait_loads();  // V_{j+1} (and the bias of tile j+1)
     wg_barrier();
+    if constexpr (BIAS)
+      if (j + 2 < ntiles) bias_issue(j + 2);
     if (active) {
+      if constexpr (BIAS) {
+        if (loader) {  // the bias of tile j+1
+          if (j + 2 < ntiles)
+            wait_loads_but<C::LOADS + BCfg::LOADS>();
+          else
+            wait_loads();
+        }
+        add_bias(j + 1, s);
+      }
       if (needs_mask(j + 1)) mask_s(j + 1, s);
       softmax(s, pb);
     }
@@ -377,6 +486,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     else
       last_step(last, 0);
     if (loader) wg_barrier();  // match group 1's extra barrier
+    if constexpr (BIAS) wait_loads();  // a wave that skipped its last bias tile
   }
 
   // Epilogue: divide by l once; LSE = ln2 * (m + log2 l). Empty row: O = 0, LSE = -inf.
@@ -399,14 +509,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int BC, bool VARLEN>
+template <int D, int BC, bool VARLEN, bool BIAS = false>
 hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
   FwdParams p = prm;
   const int total = p.BH * p.nqt;
   if (causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true, VARLEN>), dim3(total), dim3(64 * kNW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true, VARLEN, BIAS>), dim3(total), dim3(64 * kNW), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false, VARLEN>), dim3(total), dim3(64 * kNW), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false, VARLEN, BIAS>), dim3(total), dim3(64 * kNW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -422,6 +532,12 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_bf16_varlen(const FwdParams& p, int d, bool causal, hipStream_t s) {
   if (d == 128) return launch<128, 96, true>(p, causal, s);
   return launch<64, 128, true>(p, causal, s);
+}
+
+// 64-key tiles: they free the registers and LDS that the bias staging takes.
+hipError_t launch_fwd_bf16_bias(const FwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return launch<128, 64, false, true>(p, causal, s);
+  return launch<64, 64, false, true>(p, causal, s);
 }
 
 }  // namespace fa

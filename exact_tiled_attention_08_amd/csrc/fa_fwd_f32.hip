@@ -7,6 +7,11 @@
 // (A: row l%32, k = l/32; B: col l%32, k = l/32; C as in the bf16 kernel), so V is read
 // from LDS in its natural [key][d] layout and needs no transposition. Single-stage LDS:
 // this path exists for exact float32 results, not for throughput.
+//
+// Additive bias (BIAS, float32 like the inputs): added to the scaled scores before the
+// softmax ("Explain FlashAttention ...", section "Keep only the state needed for the final
+// weighted average"); each lane reads the bias of its own query row and 16 keys per tile
+// straight from global memory. Keys past Nk are not read.
 #include "fa_internal.h"
 
 namespace fa {
@@ -15,7 +20,7 @@ namespace {
 constexpr int kBC = 32;  // keys per tile
 constexpr int kNW = 4;   // waves per workgroup (32 query rows each)
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
   constexpr int PITCH = D + 4;  // floats per LDS row (4-float pad against bank conflicts)
   constexpr int T = 64 * kNW;
@@ -31,6 +36,15 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
   const float* __restrict__ qh = (const float*)p.q + (size_t)bh * p.Nq * D;
   const float* __restrict__ kh = (const float*)p.k + (size_t)bh * p.Nk * D;
   const float* __restrict__ vh = (const float*)p.v + (size_t)bh * p.Nk * D;
+  // bias row of this lane's query (clamped to Nq-1: rows past Nq are never stored)
+  const float* brow = nullptr;
+  if constexpr (BIAS) {
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+    brow = (const float*)p.bias + (size_t)b * p.bsb + (size_t)h * p.bsh +
+           (size_t)min(qrow, p.Nq - 1) * p.bsq;
+  }
+  const float cs = BIAS ? 1.f : p.c;  // with a bias, scores are turned into log2 units first
 
   // Q^T operand: element (k = 2*step + g, col = query) for every step of the contraction.
   float qv[D / 2];
@@ -71,6 +85,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
       for (int st = 0; st < D / 2; ++st)
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[col * PITCH + 2 * st + g], qv[st], s, 0, 0, 0);
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const float bv = key < p.Nk ? brow[key] : 0.f;
+          s[i] = __builtin_fmaf(s[i], p.c, bv * kLog2e);
+        }
+      }
 
       const bool need_mask = (kv0 + kBC > p.Nk) || (CAUSAL && kv0 + kBC - 1 > wq0 + p.off);
       if (need_mask) {
@@ -83,14 +105,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx * p.c);
+      const float m_new = fmaxf(m, mx * cs);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m - m_use);
       m = m_new;
       float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m_use));
+        s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -m_use));
         lsum += s[i];
       }
       l = l * alpha + lsum;
@@ -126,14 +148,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool BIAS>
 hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
   FwdParams p = prm;
   const int total = p.BH * p.nqt;
   if (causal)
-    hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3(total), dim3(64 * kNW), 0, s, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, true, BIAS>), dim3(total), dim3(64 * kNW), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3(total), dim3(64 * kNW), 0, s, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, false, BIAS>), dim3(total), dim3(64 * kNW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -142,7 +164,11 @@ hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
 int fwd_f32_block_rows(int) { return 32 * kNW; }
 
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s) {
-  return d == 128 ? launch<128>(p, causal, s) : launch<64>(p, causal, s);
+  return d == 128 ? launch<128, false>(p, causal, s) : launch<64, false>(p, causal, s);
+}
+
+hipError_t launch_fwd_f32_bias(const FwdParams& p, int d, bool causal, hipStream_t s) {
+  return d == 128 ? launch<128, true>(p, causal, s) : launch<64, true>(p, causal, s);
 }
 
 }  // namespace fa

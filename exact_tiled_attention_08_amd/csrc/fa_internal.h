@@ -39,6 +39,12 @@ struct FwdParams {
   int total_q;
   int total_k;
   int top_left;   // causal queries at the start of each sequence's keys (else at the end)
+  // Additive bias only: element (b, h, i, j) at bias[b*bsb + h*bsh + i*bsq + j], in the
+  // input dtype (a stride of 0 repeats a dimension); H above gives b and h of a pair.
+  const void* bias;
+  long long bsb;
+  long long bsh;
+  long long bsq;
 };
 
 struct DecodeParams {
@@ -101,6 +107,13 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory loads are still in flight (loads
+// complete in issue order, so the ones issued before the last N have landed).
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // One global_load_lds_dwordx4: each lane copies 16 bytes from (uniform base + its 32-bit
 // byte offset) to LDS byte address lds_base + 16*lane (lds_base wave-uniform, in M0).
@@ -124,6 +137,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 // Launchers (defined next to their kernels). Each returns the hipError_t of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_bf16_varlen(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_fwd_bf16_bias(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_fwd_f32_bias(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, hipStream_t s);
 int fwd_fp8_block_rows();
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);

@@ -60,7 +60,7 @@ typedef enum {
   FA_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than required             */
   FA_ERR_HIP = -5,          /* the HIP runtime reported an error at launch         */
   FA_ERR_VALUE = -6,        /* scale not finite and > 0, causal not 0/1/2, ...     */
-  FA_ERR_ALIGN = -7         /* a tensor pointer is not 16-byte aligned             */
+  FA_ERR_ALIGN = -7         /* a tensor pointer or bias stride is not aligned      */
 } fa_status;
 
 typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
@@ -79,6 +79,30 @@ typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
 fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
                  fa_dtype dtype, void* stream);
+
+/*
+ * fa_fwd_bias — fa_fwd with an additive bias on the scaled scores ("Explain
+ * FlashAttention ...", section "Keep only the state needed for the final weighted average":
+ * the scores are scaled, then the intended mask or bias is added, then the softmax):
+ *     S[b][h][i][j] = scale * q_i . k_j + bias[b*stride_b + h*stride_h + i*stride_q + j]
+ *   bias: dtype elements (bfloat16 or float32, like q, k, v), keys contiguous; strides in
+ *   elements, each >= 0 (0 repeats the same values along that dimension, e.g. one [Nq][Nk]
+ *   bias for every (b, h), or a [B][Nk] key-padding bias with stride_h = stride_q = 0).
+ *   The bias is not multiplied by scale. A key hidden by the causal mask stays hidden
+ *   whatever its bias; a bias of -inf hides a key (a row whose keys are all hidden gets
+ *   O = 0 and LSE = -inf); +inf and NaN are outside the contract. LSE is that of the
+ *   scaled, biased, masked scores.
+ *   FA_BF16: the bias pointer must be 16-byte aligned and the three strides multiples of
+ *   8; each bias row is read in 16-byte pieces, so its first Nk elements rounded up to a
+ *   multiple of 8 must be readable (pad the key dimension of the allocation to a multiple
+ *   of 8). The bias of rows and keys that are masked may be read but never matters.
+ *   FA_F32: 4-byte alignment; only the first Nk elements of each row are read.
+ *   stride_q * 64 < 2^31. Other arguments, sizes and errors as in fa_fwd.
+ */
+fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      float* o, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                      int causal, fa_dtype dtype, void* stream);
 
 /*
  * fa_fwd_fp8 — fa_fwd with 8-bit floating-point inputs on the FP8 matrix cores ("FlashAttention:

@@ -235,3 +235,41 @@ def _fp8(**kw):
 ])
 def test_fp8_rejects(kw, status):
     assert _fp8(**kw) == status
+
+
+def _bias(**kw):
+    a = dict(q=P, k=P, v=P, bias=P, sb=0, sh=0, sq=64, o=P, lse=P, B=1, H=1, Nq=16, Nk=16, d=64,
+             scale=0.125, causal=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_fwd_bias(a["q"], a["k"], a["v"], a["bias"], a["sb"], a["sh"], a["sq"],
+                                    a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                    a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bias=None), fa.FA_ERR_NULL),
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(Nk=0), fa.FA_ERR_SHAPE),
+    (dict(sq=-8), fa.FA_ERR_SHAPE),
+    (dict(sb=-1), fa.FA_ERR_SHAPE),
+    (dict(sh=1 << 62), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(sq=1 << 25), fa.FA_ERR_UNSUPPORTED),   # 32 rows of it exceed 32-bit byte offsets
+    (dict(causal=3), fa.FA_ERR_VALUE),
+    (dict(scale=0.0), fa.FA_ERR_VALUE),
+    (dict(bias=P + 8), fa.FA_ERR_ALIGN),          # bfloat16 bias rows are read 16 bytes at a time
+    (dict(sq=20), fa.FA_ERR_ALIGN),
+    (dict(sh=4), fa.FA_ERR_ALIGN),
+    (dict(dtype=fa.FA_F32, bias=P + 2), fa.FA_ERR_ALIGN),
+])
+def test_bias_rejects(kw, status):
+    assert _bias(**kw) == status
+
+
+def test_bias_python_layer_checks_without_gpu():
+    """The binding refuses CPU tensors before it calls the library."""
+    import torch
+    x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd_bias(x, x, x, torch.zeros((8, 8), dtype=torch.bfloat16))

@@ -128,6 +128,13 @@ def make_inputs_fp8(w: Workload, device="cpu"):
     return tuple(out)
 
 
+def make_bias(w: Workload, device="cpu", mult: float = 2.0):
+    """The additive bias of the biased prefill on workload w: a full [B, H, Nq, Nk] tensor of
+    w's dtype, N(0,1) * mult drawn as in `draw` with seed 10c + 4 (one value per (b, h, query,
+    key): the general case, nothing shared or broadcast)."""
+    return draw((w.B, w.H, w.Nq, w.Nk), 10 * w.number + 4, mult, w.dtype, device)
+
+
 def make_grad(w: Workload, device="cpu"):
     """dO, the gradient fed to the backward pass: N(0,1) of q's shape and dtype, seed 10c + 3."""
     return draw((w.B, w.H, w.Nq, w.d), 10 * w.number + 3, 1.0, w.dtype, device)
