@@ -138,6 +138,7 @@ fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const void* b
   p.nqt = (int)nqt;
   p.hpg = heads_per_group((int)BH, nqt);
   p.c = scale * fa::kLog2e;
+  p.scale = scale;
   p.H = H;
   p.bias = bias;
   p.bsb = bias_stride_b;

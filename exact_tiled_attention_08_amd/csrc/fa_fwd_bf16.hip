@@ -49,8 +49,10 @@
 // j+1, and waits for exactly the loads it needs (loads complete in issue order), so the
 // K/V stream is never held up behind the bias. Rows are stored with the 16-byte chunk
 // index XORed with (row / 2) % 8, which leaves at most two lanes of a half-wave on one
-// bank pair when each lane reads its row's 4 keys. In log2 units the score becomes
-// s * scale * log2(e) + bias * log2(e); masked keys stay -inf whatever their bias.
+// bank pair when each lane reads its row's 4 keys. The score becomes s * scale + bias
+// (one fma after widening the bias) and the softmax takes it to log2 units with its own
+// fma, so the bias costs two vector ops per score; masked keys stay -inf whatever their
+// bias.
 //
 // Rescaling: the offset is always the exact running max, so the largest weight of a row
 // is exactly 1 and survives the rounding of P to bfloat16 without error (an offset that
@@ -257,8 +259,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
       dma16(base, (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)ch, lds);
     }
   };
-  // s <- s * scale * log2(e) + bias * log2(e) for tile t (this lane's query row, its 16
-  // keys per 32-key block: 32kb + 8(i/4) + 4g + i%4, one 8-byte read per 4 keys).
+  // s <- s * scale + bias for tile t (this lane's query row, its 16 keys per 32-key
+  // block: 32kb + 8(i/4) + 4g + i%4, one 8-byte read per 4 keys).
   auto add_bias = [&](int t, f32x16 (&s)[BC / 32]) {
     const char* row = bias_buf(t) + col * BCfg::ROWB;
     const int sw = (col >> 1) & 7;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float bv = __uint_as_float((uint32_t)(uint16_t)raw[e] << 16);
-          s[kb][4 * qd + e] = __builtin_fmaf(s[kb][4 * qd + e], p.c, bv * kLog2e);
+          s[kb][4 * qd + e] = __builtin_fmaf(s[kb][4 * qd + e], p.scale, bv);
         }
       }
   };
@@ -305,8 +307,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // Online softmax of one tile; O is rescaled here, after the previous tile's PV and
   // before this tile's, and only when some row of the wave raised its max. With a bias
-  // the scores arrive already in log2 units.
-  const float cs = BIAS ? 1.f : p.c;
+  // the scores arrive already scaled (natural-log units).
+  const float cs = BIAS ? kLog2e : p.c;
   auto softmax = [&](f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16]) {
     float mx = -INFINITY;
 #pragma unroll

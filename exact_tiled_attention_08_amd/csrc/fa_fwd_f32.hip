@@ -44,7 +44,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
     brow = (const float*)p.bias + (size_t)b * p.bsb + (size_t)h * p.bsh +
            (size_t)min(qrow, p.Nq - 1) * p.bsq;
   }
-  const float cs = BIAS ? 1.f : p.c;  // with a bias, scores are turned into log2 units first
+  const float cs = BIAS ? kLog2e : p.c;  // with a bias, scores arrive scaled (s * scale + bias)
 
   // Q^T operand: element (k = 2*step + g, col = query) for every step of the contraction.
   float qv[D / 2];
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_f32_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
           const float bv = key < p.Nk ? brow[key] : 0.f;
-          s[i] = __builtin_fmaf(s[i], p.c, bv * kLog2e);
+          s[i] = __builtin_fmaf(s[i], p.scale, bv);
         }
       }
 

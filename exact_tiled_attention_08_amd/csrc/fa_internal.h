@@ -29,6 +29,7 @@ struct FwdParams {
   int nqt;        // number of query tiles per (b, h)
   int hpg;        // (b, h) pairs per XCD group for the block -> tile mapping
   float c;        // scale * log2(e): scores are exponentiated base 2 (FP8: times both descales)
+  float scale;    // additive bias only: the softmax scale itself
   float vscale;   // FP8 only: the descale factor of v
   // Packed variable-length batches only: q, k, v, o are [total][H][d], lse [H][total_q];
   // sequence b owns rows cu_q[b] .. cu_q[b+1]-1 (queries) and cu_k[b] .. cu_k[b+1]-1 (keys).
