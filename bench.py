@@ -160,7 +160,7 @@ def bias_record(num: int, steps: int, warmup: int):
         "ms_per_step": wall_ms, "kernel_ms": ev_ms,
         "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for("fwd_bf16_bias", num)},
     }
     del q, k, v, bias, o, lse
     torch.cuda.empty_cache()
@@ -188,7 +188,7 @@ def fp8_record(num: int, steps: int, warmup: int):
         "flops_per_launch": w.flops, "ms_per_step": wall_ms, "kernel_ms": ev_ms,
         "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic_for("fwd_fp8", num)},
     }
     del q8, k8, v8, o, lse
     torch.cuda.empty_cache()
@@ -218,7 +218,8 @@ def varlen_record(steps: int, warmup: int):
         "lengths": lens, "flops_per_launch": flops, "ms_per_step": wall_ms, "kernel_ms": ev_ms,
         "tflops": flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_for("fwd_bf16_varlen", "varlen")},
     }
     del q, k, v, o, lse
     torch.cuda.empty_cache()
@@ -322,7 +323,7 @@ def paged_decode_record(steps: int, warmup: int, page_size: int = 64):
         "page_size": page_size, "bytes_per_call": nbytes, "ms_per_step": wall_ms,
         "kernel_ms": ev_ms, "note": "kernel_ms spans both launches of one call (split + merge)",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for("decode_paged", 5)},
     }
     del q, kc, vc
     torch.cuda.empty_cache()

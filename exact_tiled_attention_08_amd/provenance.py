@@ -13,8 +13,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 KERNEL_SOURCES = {
     "fwd_bf16": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
+    "fwd_bf16_bias": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
+    "fwd_bf16_varlen": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
+    "fwd_fp8": ["csrc/fa_fwd_fp8.hip", "csrc/fa_internal.h"],
     "fwd_f32": ["csrc/fa_fwd_f32.hip", "csrc/fa_internal.h"],
     "decode": ["csrc/fa_decode.hip", "csrc/fa_internal.h"],
+    "decode_paged": ["csrc/fa_decode.hip", "csrc/fa_internal.h"],
     "bwd_pre": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
     "bwd_dkdv": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
     "bwd_dq": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],

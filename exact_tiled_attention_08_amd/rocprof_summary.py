@@ -117,7 +117,7 @@ def traffic_main(argv):
     from exact_tiled_attention_08_amd.provenance import source_hash
     ap = argparse.ArgumentParser(prog="rocprof_summary traffic")
     ap.add_argument("--kind", required=True)
-    ap.add_argument("--workload", type=int, required=True)
+    ap.add_argument("--workload", required=True, help="workload number, or a name such as 'varlen'")
     ap.add_argument("--match", required=True)
     ap.add_argument("--kernel-fetch", required=True)
     ap.add_argument("--kernel-write", required=True)
