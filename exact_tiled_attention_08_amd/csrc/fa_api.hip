@@ -341,7 +341,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
   const long long BH = (long long)B * H;
   if (BH > INT32_MAX) return FA_ERR_SHAPE;
-  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
@@ -378,6 +378,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   p.scale = scale;
   p.c = scale * fa::kLog2e;
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  if (dtype == FA_F32) return finish_launch(fa::launch_bwd_f32(p, d, causal != 0, (hipStream_t)stream));
   return finish_launch(fa::launch_bwd(p, d, causal != 0, (hipStream_t)stream));
 }
 

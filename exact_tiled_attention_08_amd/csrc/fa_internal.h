@@ -146,6 +146,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s)
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 // Query rows per workgroup of each prefill kernel (host needs it for the grid).
 int fwd_bf16_block_rows(int d);

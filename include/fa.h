@@ -217,11 +217,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
  *   dq    [B][H][Nq][d]  float32, dk, dv [B][H][Nk][d] float32 (written; every element)
  *   workspace: device memory of at least fa_bwd_workspace_bytes(B, H, Nq) bytes, 16-byte
  *   aligned, owned by the caller; contents on entry are ignored, on return unspecified.
- *   dtype: FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). d in {64, 128}; B, H, Nq, Nk >= 1;
+ *   dtype: FA_BF16 or FA_F32 (q, k, v and do share it). d in {64, 128}; B, H, Nq, Nk >= 1;
  *   Nq * d, Nk * d <= 2^30. scale finite and > 0; causal 0, 1 or 2 (the alignments of
  *   fa_fwd). lse only needs 4-byte alignment. Three kernels run in order on `stream`;
- *   every output element is written exactly once (deterministic, no atomics). P and dS are
- *   rounded to bfloat16 as MFMA operands; everything else is float32.
+ *   every output element is written exactly once (deterministic, no atomics). FA_BF16: P
+ *   and dS are rounded to bfloat16 as MFMA operands, everything else is float32. FA_F32:
+ *   float32 MFMA throughout, nothing is rounded below float32.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
                  const void* dout, float* dq, float* dk, float* dv, int B, int H, int Nq, int Nk,

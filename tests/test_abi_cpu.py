@@ -144,7 +144,7 @@ def _bwd(**kw):
     (dict(do=None), fa.FA_ERR_NULL), (dict(dq=None), fa.FA_ERR_NULL), (dict(dk=None), fa.FA_ERR_NULL),
     (dict(dv=None), fa.FA_ERR_NULL),
     (dict(B=0), fa.FA_ERR_SHAPE), (dict(Nq=0), fa.FA_ERR_SHAPE), (dict(Nk=-1), fa.FA_ERR_SHAPE),
-    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(Nk=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(scale=float("inf")), fa.FA_ERR_VALUE),
     (dict(causal=-1), fa.FA_ERR_VALUE),

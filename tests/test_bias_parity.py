@@ -151,3 +151,22 @@ def test_bias_workload_sampled():
                                     bias=bias.cpu())
     st = compare(rows_of(o, rows, w.d), rows_of(lse, rows), o_ref, l_ref, w.dtype, "bias workload")
     say(f"  {st}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_bias_overwrites_outputs_and_is_deterministic(dtype):
+    """NaN-prefilled O and LSE are fully overwritten, and two calls agree bit for bit."""
+    q = seeded((2, 3, 300, 128), 2951, dtype, mult=2.0)
+    k = seeded((2, 3, 333, 128), 2952, dtype, mult=2.0)
+    v = seeded((2, 3, 333, 128), 2953, dtype)
+    bias = fa.pad_bias(_bias("full", 2, 3, 300, 333, 2954, dtype))
+    outs = []
+    for _ in range(2):
+        o = torch.full((2, 3, 300, 128), float("nan"), device=DEV)
+        lse = torch.full((2, 3, 300), float("nan"), device=DEV)
+        say(f"bias NaN-prefilled outputs {dtype}")
+        fa.fwd_bias(q, k, v, bias, causal=1, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and not torch.isnan(lse).any()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
