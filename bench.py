@@ -73,6 +73,49 @@ def time_launches(fn, steps: int, warmup: int):
     return wall, start.elapsed_time(stop) / steps
 
 
+def clock_under_load(step, seconds: float = 2.0):
+    """Shader clock while `step` runs back to back: a thread samples `amd-smi metric -c`
+    (the current gfx clock of each XCD, averaged) as a child process while this process
+    keeps the GPU busy for about `seconds`. Outside any timed region. Returns a dict, or
+    None if amd-smi gives nothing."""
+    import subprocess
+    import threading
+    import torch
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-c", "--json", "-g", "0"],
+                                   capture_output=True, text=True, timeout=30)
+                data = json.loads(r.stdout)
+                gpus = data["gpu_data"] if isinstance(data, dict) else data
+                clk = gpus[0]["clock"]
+                vals = [v["clk"]["value"] for key, v in clk.items()
+                        if key.startswith("gfx") and isinstance(v, dict) and "clk" in v]
+                if vals:
+                    samples.append(sum(vals) / len(vals))
+            except (OSError, ValueError, KeyError, IndexError, TypeError,
+                    subprocess.SubprocessError):
+                return
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.time()
+    th.start()
+    while time.time() - t0 < seconds or (not samples and th.is_alive() and time.time() - t0 < 4 * seconds):
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    if not samples:
+        return None
+    return {"sclk_mhz": sum(samples) / len(samples), "samples": len(samples),
+            "source": "amd-smi metric -c: current gfx clock averaged over the XCDs, sampled "
+                      "while the headline prefill ran back to back (outside the timed steps)"}
+
+
 def cpu_baseline(w, q, k, v, target_s: float):
     """Time the oracle on a row sample sized for about target_s seconds; report the
     algorithmic rate (same FLOP convention as the GPU figure)."""
@@ -119,7 +162,7 @@ def prefill_record(num: int, steps: int, warmup: int):
     wall_ms, ev_ms = time_launches(step, steps, warmup)
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
-    rec = {
+    rec = {"step": step,
         "workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
         "causal": w.causal, "flops_per_launch": w.flops,
         "ms_per_step": wall_ms, "kernel_ms": ev_ms,
@@ -390,9 +433,17 @@ def main():
         return
 
     main_rec, (w, q, k, v) = prefill_record(args.workload, args.steps, args.warmup)
+    main_step = main_rec.pop("step")
     if args.only == "prefill":
         print(json.dumps({"prefill": main_rec}), flush=True)
         return
+    # context for the roofline, measured after the timed steps: the practical MFMA rate of
+    # this box (fa_probe_mfma) and the shader clock while the headline kernel runs
+    import exact_tiled_attention_08_amd as fa
+    probe_tf = fa.probe_mfma()
+    main_rec["roofline"]["measured_mfma_peak"] = probe_tf
+    main_rec["roofline"]["frac_of_measured_mfma_peak"] = main_rec["roofline"]["achieved"] / probe_tf
+    clock = clock_under_load(main_step) if args.only is None else None
     out = {
         "metric": METRIC,
         "value": main_rec["tflops"],
@@ -410,6 +461,10 @@ def main():
                    "causal": w.causal, "global_batch": w.B, "seq_len": w.Nq, "parallelism": "none"},
         "roofline": main_rec["roofline"],
         "kernel_ms": main_rec["kernel_ms"],
+        "mfma_probe": {"tflops": probe_tf, "frac_of_peak": probe_tf / PEAK_BF16_TFLOPS,
+                       "what": "fa_probe_mfma: back-to-back bf16 32x32x16 MFMAs on register "
+                               "operands, no memory traffic, 2048 workgroups x 4 waves"},
+        "clock": clock,
     }
     if args.only is None and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
@@ -418,6 +473,7 @@ def main():
     if args.only is None and not args.no_extra:
         extra = {}
         rec4, _ = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
+        rec4.pop("step")
         extra["prefill_N30000"] = rec4
         torch.cuda.empty_cache()
         extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))

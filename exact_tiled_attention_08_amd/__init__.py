@@ -35,7 +35,7 @@ FA_BF16, FA_F32 = 0, 1
 
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_bias", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_hip_error",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_probe_mfma", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -53,6 +53,7 @@ _SIGS = {
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _sz, _i, _vp]),
+    "fa_probe_mfma": (_i, [_vp, _sz, _i, _i, _vp]),
     "fa_status_str": (ctypes.c_char_p, [_i]),
     "fa_last_hip_error": (_i, []),
     "fa_last_hip_error_str": (ctypes.c_char_p, []),
@@ -96,6 +97,27 @@ def library():
 
 def status_str(status: int) -> str:
     return library().fa_status_str(int(status)).decode()
+
+
+def probe_mfma(blocks: int = 2048, iters: int = 2000, reps: int = 3) -> float:
+    """Practical dense bf16 MFMA rate of the current GPU in TFLOP/s: times fa_probe_mfma
+    (back-to-back 32x32x16 MFMAs on register operands, no memory traffic) with events on
+    the current stream and returns the best of `reps` launches. Measurement aid only."""
+    import torch
+    sink = torch.empty((blocks * 256,), dtype=torch.float32, device="cuda")
+    st = _stream_ptr(sink.device)
+    lib = library()
+    _raise(lib.fa_probe_mfma(sink.data_ptr(), sink.numel() * 4, blocks, 1, st), "fa_probe_mfma")
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _raise(lib.fa_probe_mfma(sink.data_ptr(), sink.numel() * 4, blocks, iters, st), "fa_probe_mfma")
+        e1.record()
+        torch.cuda.synchronize()
+        flops = blocks * 4 * iters * 4 * 32768.0
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
 
 
 def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_bwd.hip",
-           "fa_bwd_f32.hip", "fa_fwd_fp8.hip"]
+           "fa_bwd_f32.hip", "fa_fwd_fp8.hip", "fa_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

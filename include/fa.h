@@ -229,6 +229,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
                  int d, float scale, int causal, void* workspace, size_t workspace_bytes,
                  fa_dtype dtype, void* stream);
 
+/*
+ * fa_probe_mfma — measurement aid, not part of the attention method: launches `blocks`
+ * workgroups of 256 threads in which every wave issues 4 * iters back-to-back
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on register operands, with no memory traffic,
+ * and writes one float per thread to `sink` (device memory of at least blocks * 1024 bytes,
+ * 4-byte aligned; its values are meaningless). Timing the launch gives the practical
+ * dense bf16 MFMA rate of the device at its current clock, the context for the attention
+ * kernels' own rate. Errors: FA_ERR_NULL, FA_ERR_SHAPE (blocks or iters < 1),
+ * FA_ERR_WORKSPACE (sink too small), FA_ERR_ALIGN, FA_ERR_HIP.
+ */
+fa_status fa_probe_mfma(float* sink, size_t sink_bytes, int blocks, int iters, void* stream);
+
 /* fa_status_str — static English description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

@@ -273,3 +273,14 @@ def test_bias_python_layer_checks_without_gpu():
     x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd_bias(x, x, x, torch.zeros((8, 8), dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1 << 20, 4, 10), fa.FA_ERR_NULL),
+    ((P, 1 << 20, 0, 10), fa.FA_ERR_SHAPE),
+    ((P, 1 << 20, 4, 0), fa.FA_ERR_SHAPE),
+    ((P, 4 * 1024 - 1, 4, 10), fa.FA_ERR_WORKSPACE),
+    ((P + 2, 1 << 20, 4, 10), fa.FA_ERR_ALIGN),
+])
+def test_probe_mfma_rejects(args, status):
+    assert fa.library().fa_probe_mfma(*args, None) == status
