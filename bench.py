@@ -55,22 +55,34 @@ def bwd_traffic(workload: int):
     return None if any(p is None for p in parts) else sum(parts)
 
 
-def time_launches(fn, steps: int, warmup: int):
-    """(wall ms per step, event ms per launch). fn launches on torch's current stream."""
+LAST_REPS = {}  # per-block event times of the latest time_launches call
+
+
+def time_launches(fn, steps: int, warmup: int, blocks: int = 5):
+    """(wall ms per step, event ms per launch). fn launches on torch's current stream.
+
+    Events are also recorded between `blocks` equal blocks of the timed steps (on the same
+    stream, with no synchronisation inside the timed region); the per-launch time of each
+    block goes to LAST_REPS["block_ms"] and their median to LAST_REPS["median_ms"]."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    nb = max(1, min(blocks, steps))
+    edges = [round(i * steps / nb) for i in range(nb + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
-        fn()
-    stop.record()
+    ev[0].record()
+    for b in range(nb):
+        for _ in range(edges[b + 1] - edges[b]):
+            fn()
+        ev[b + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, start.elapsed_time(stop) / steps
+    per = [ev[b].elapsed_time(ev[b + 1]) / (edges[b + 1] - edges[b]) for b in range(nb)]
+    LAST_REPS.clear()
+    LAST_REPS.update({"block_ms": per, "median_ms": sorted(per)[len(per) // 2]})
+    return wall, ev[0].elapsed_time(ev[nb]) / steps
 
 
 def clock_under_load(step, seconds: float = 2.0):
@@ -142,9 +154,12 @@ def cpu_baseline(w, q, k, v, target_s: float):
     oracle.attention(qc, kc, vc, w.scale, w.causal, rows=rows, threads=threads)
     sec = time.perf_counter() - t0
     flops = row_flops(rows)
+    # the whole workload at the sample's rate: time scales with the visible keys of the rows
+    full_s = sec * row_flops(np.arange(total_rows)) / flops
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {total_rows} query rows (uniform random, seed 0) of the same "
-                      f"workload, all their visible keys; {flops / 1e9:.1f} GFLOP in {sec:.1f} s"}
+                      f"workload, all their visible keys; {flops / 1e9:.1f} GFLOP in {sec:.1f} s",
+            "extrapolated_full_workload_s": full_s}
 
 
 def prefill_record(num: int, steps: int, warmup: int):
@@ -160,9 +175,11 @@ def prefill_record(num: int, steps: int, warmup: int):
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
     wall_ms, ev_ms = time_launches(step, steps, warmup)
+    reps = dict(LAST_REPS)
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
-    rec = {"step": step,
+    rec = {"step": step, "kernel_ms_blocks": reps["block_ms"],
+           "kernel_ms_median_of_blocks": reps["median_ms"],
         "workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
         "causal": w.causal, "flops_per_launch": w.flops,
         "ms_per_step": wall_ms, "kernel_ms": ev_ms,
@@ -461,6 +478,8 @@ def main():
                    "causal": w.causal, "global_batch": w.B, "seq_len": w.Nq, "parallelism": "none"},
         "roofline": main_rec["roofline"],
         "kernel_ms": main_rec["kernel_ms"],
+        "kernel_ms_median_of_blocks": main_rec["kernel_ms_median_of_blocks"],
+        "kernel_ms_blocks": main_rec["kernel_ms_blocks"],
         "mfma_probe": {"tflops": probe_tf, "frac_of_peak": probe_tf / PEAK_BF16_TFLOPS,
                        "what": "fa_probe_mfma: back-to-back bf16 32x32x16 MFMAs on register "
                                "operands, no memory traffic, 2048 workgroups x 4 waves"},
