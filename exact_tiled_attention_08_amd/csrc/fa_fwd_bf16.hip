@@ -58,6 +58,8 @@
 // is exactly 1 and survives the rounding of P to bfloat16 without error (an offset that
 // lags the max would leave the dominant weight at 2^delta, rounded by up to 2^-9 of its
 // size); the multiply of O is skipped when no row of the wave raised its max.
+#include <utility>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -249,9 +251,21 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     const int row = min(lrow + n * C::ROWSTEP, Nk - 1 - kv0);
     dma16((const char*)lbase + (size_t)kv0 * rs * 2, (uint32_t)(row * rs * 2) + lchunk, lds);
   };
+  // Whole tiles (every row below Nk) need no clamp: the lane's offset from its row-group
+  // base is then the same for every slot and tile (one loop-invariant VGPR) and the row
+  // step goes into the scalar base, so issuing a load costs no vector instruction.
+  const uint32_t loff = (uint32_t)(lrow * rs * 2) + lchunk;
   auto issue = [&](int t, char* dst) {
+    const int kv0 = t * BC;
+    if (kv0 + BC <= Nk) {
+      const uint32_t lds0 = (uint32_t)(uintptr_t)((lds_char*)(dst + 64 * wg4 * 16));
+      [&]<int... N>(std::integer_sequence<int, N...>) {
+        (dma16_at<N * C::TL * 16>((const char*)lbase + (size_t)(kv0 + N * C::ROWSTEP) * rs * 2, loff, lds0), ...);
+      }(std::make_integer_sequence<int, C::LOADS>{});
+    } else {
 #pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) dma(t, dst, n);
+      for (int n = 0; n < C::LOADS; ++n) dma(t, dst, n);  // the key tail: rows clamped
+    }
   };
   // Bias of key tile t into this wave's buffer t % 2. Direct load n of lane L fills LDS
   // slot 64n + L: row 8n + L/8, chunk position L%8, which holds the row's chunk
@@ -260,11 +274,28 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // row's first Nk elements rounded up to a multiple of 8.
   char* const bias_lds = smem + C::LDS;
   auto bias_buf = [&](int t) { return bias_lds + ((t & 1) * kNW + w) * BCfg::WAVEB; };
+  // Lane offsets of whole tiles (no chunk starts at or past Nk) do not depend on the
+  // tile: computed once.
+  uint32_t boff[BCfg::LOADS];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int n = 0; n < BCfg::LOADS; ++n) {
+      const int dr = min(wq0 + 8 * n + (lane >> 3), Nq - 1) - bias_r0;
+      const int ch = (lane & 7) ^ (((n & 1) << 2) | (lane >> 4));
+      boff[n] = (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)ch;
+    }
+  }
   auto bias_issue = [&](int t) {
     const int kv0 = t * BC;
     const int cmax = (Nk - 1 - kv0) >> 3;
     const char* base = (const char*)(bw + kv0);
     char* dst = bias_buf(t);
+    if (kv0 + BC <= Nk) {
+#pragma unroll
+      for (int n = 0; n < BCfg::LOADS; ++n)
+        dma16_once(base, boff[n], (uint32_t)(uintptr_t)((lds_char*)(dst + n * 64 * 16)));
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < BCfg::LOADS; ++n) {
       const int row = 8 * n + (lane >> 3);

@@ -26,6 +26,8 @@
 //   lanes, lane t receives byte t%8 of the 8-byte chunks that lanes 2j + (t%16)/8 address,
 //   j = 0..7; each lane addresses the chunk of one key row that holds its group's dims).
 // Both products use the same k order for A and B, which is all the instruction requires.
+#include <utility>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -127,8 +129,18 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
   const int wg4 = w & 3;
   auto kbuf = [&](int i) -> char* { return smem + i * TILEB; };
   auto vbuf = [&](int i) -> char* { return smem + (2 + i) * TILEB; };
+  // Whole tiles need no row clamp: one loop-invariant lane offset, the row step in the
+  // scalar base and the slot in the LDS base (no vector instruction per load).
+  const uint32_t loff = (uint32_t)(lrow * ROWB) + lchunk;
   auto issue = [&](int t, char* dst) {
     const int kv0 = t * BC;
+    if (kv0 + BC <= Nk) {
+      const uint32_t lds0 = (uint32_t)(uintptr_t)((lds_char*)(dst + 64 * wg4 * 16));
+      [&]<int... N>(std::integer_sequence<int, N...>) {
+        (dma16_at<N * TL * 16>(lbase + (size_t)(kv0 + N * ROWSTEP) * ROWB, loff, lds0), ...);
+      }(std::make_integer_sequence<int, LOADS>{});
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
       const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * TL + 64 * wg4) * 16));

@@ -135,6 +135,22 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
       : "memory");
 }
 
+// dma16 to LDS byte address lds_base + IMM: the constant is added to M0 inside the copy, so
+// the slots of one buffer need one scalar base between them (the compiler would otherwise
+// keep one scalar per slot alive across the loop and spill them to vector registers).
+template <int IMM>
+__device__ __forceinline__ void dma16_at(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %3, %4\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base), "i"(IMM)
+      : "memory", "scc");
+}
+
 // Launchers (defined next to their kernels). Each returns the hipError_t of the launch.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_bf16_varlen(const FwdParams& p, int d, bool causal, hipStream_t s);

@@ -223,8 +223,9 @@ def test_bwd_python_layer_rejects_on_gpu():
     q = torch.zeros((1, 1, 4, 64), dtype=torch.float32, device=DEV)
     o = torch.zeros((1, 1, 4, 64), dtype=torch.float32, device=DEV)
     lse = torch.zeros((1, 1, 4), dtype=torch.float32, device=DEV)
-    with pytest.raises(NotImplementedError):
-        fa.bwd(q, q, q, o, lse, q)                 # float32 backward is not provided
+    q96 = torch.zeros((1, 1, 4, 96), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(NotImplementedError):       # head size 96 is not provided
+        fa.bwd(q96, q96, q96, torch.zeros((1, 1, 4, 96), device=DEV), lse, q96)
     qb = q.to(torch.bfloat16)
     with pytest.raises(ValueError):
         fa.bwd(qb, qb, qb, o, lse, q)              # dO dtype differs from q
