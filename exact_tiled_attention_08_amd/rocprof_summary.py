@@ -56,10 +56,12 @@ def counter_rows(db: str):
     return [dict(zip(cols, r)) for r in rows]
 
 
-def summarise(dbs, match: str | None, wgs: int | None = None):
+def summarise(dbs, match: str | None, wgs: int | None = None, calls: tuple | None = None):
+    """calls=(a, b): keep only dispatches a .. b-1 of each kernel and launch shape, in
+    dispatch order (e.g. the timed launches after the warm-up ones)."""
     by = {}
     for db in dbs:
-        for name, dur, grid, wg, lds, vgpr, agpr, _ in kernel_rows(db):
+        for name, dur, grid, wg, lds, vgpr, agpr, did in kernel_rows(db):
             if match and match not in name:
                 continue
             if wgs is not None and grid // max(1, wg) != wgs:
@@ -67,7 +69,13 @@ def summarise(dbs, match: str | None, wgs: int | None = None):
             key = (_short(name), grid // max(1, wg))  # one row per kernel and launch shape
             ent = by.setdefault(key, {"d": [], "grid": grid, "wg": wg, "lds": lds,
                                       "vgpr": vgpr, "agpr": agpr})
-            ent["d"].append(dur)
+            ent["d"].append((did, dur))
+    for ent in by.values():
+        ent["d"].sort()
+        if calls is not None:
+            ent["d"] = ent["d"][calls[0]:calls[1]]
+        ent["d"] = [dur for _, dur in ent["d"]]
+    by = {k: e for k, e in by.items() if e["d"]}
     counters = {}
     for db in dbs:
         for r in counter_rows(db):
@@ -236,9 +244,16 @@ def main():
     ap.add_argument("--command", required=True, help="the command that produced the database")
     ap.add_argument("--match", default=None, help="keep kernels whose name contains this")
     ap.add_argument("--wgs", type=int, default=None, help="keep launches of this many workgroups")
+    ap.add_argument("--calls", default=None,
+                    help="A:B keeps dispatches A .. B-1 of each kernel, in dispatch order")
     args = ap.parse_args()
-    by, counters = summarise(args.dbs, args.match, args.wgs)
-    print(render(by, counters, args.command))
+    calls = tuple(int(x) for x in args.calls.split(":")) if args.calls else None
+    by, counters = summarise(args.dbs, args.match, args.wgs, calls)
+    text = render(by, counters, args.command)
+    if calls:
+        text = text.replace("| kernel | calls |", f"Dispatches {calls[0]} .. {calls[1] - 1} of each kernel "
+                            "(in dispatch order) only.\n\n| kernel | calls |", 1)
+    print(text)
 
 
 if __name__ == "__main__":
