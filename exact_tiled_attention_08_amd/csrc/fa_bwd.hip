@@ -219,6 +219,10 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   for (int db = 0; db < D / 32; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
+    // The accumulators live in the matrix registers (AGPRs) from here to the end of the
+    // loops; without this and the pin after every tile the compiler keeps them in VGPRs at
+    // the loop edge and copies all 128 of them out and back in every tile.
+    asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
   }
 
   // One 64-query tile as a single stream of 4*NG MFMAs (NG = D/8 per group):
@@ -230,7 +234,9 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   // (P = exp2(S c - LSE2), dS = P (dP - D), rounding to bfloat16) is spread over group 1's
   // MFMAs and that of step 1 over group 2's, so the matrix core and the vector ALU of the
   // SIMD work at the same time.
-  auto tile_stream = [&](const char* Qs, const char* dOs, const float* sts, const f32x16 (&sinit)[2]) {
+  auto tile_stream = [&](auto maskedc, const char* Qs, const char* dOs, const float* sts,
+                         const f32x16 (&sinit)[2]) {
+    constexpr bool MASKED = decltype(maskedc)::value;
     constexpr int NG = D / 8, NF = 4 * NG, RING = 6, EPM = 16 / NG;  // elements per MFMA
     f32x16 s[2], dp[2];
     bf16x8 pb[2][2], dsb[2][2];
@@ -250,12 +256,20 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
       L[j & 1] = *(const f32x4*)(sts + 32 * x + 8 * j + 4 * g);
       Dv[j & 1] = *(const f32x4*)(sts + 64 + 32 * x + 8 * j + 4 * g);
     };
-    auto elem = [&](auto xc, auto ec) {
-      constexpr int x = decltype(xc)::value, e = decltype(ec)::value;
-      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x][e], p.c, -L[(e >> 2) & 1][e & 3]));
-      const float ds = pe * (dp[x][e] - Dv[(e >> 2) & 1][e & 3]);
+    // The float32 work of one element is split over two MFMA slots: the exponential and
+    // dP - D in one, the product and the bfloat16 roundings in the next, so that no
+    // instruction waits for the exponential it follows.
+    float pe_t[2][EPM], sd_t[2][EPM];
+    auto front = [&](auto xc, auto ec, auto bc) {
+      constexpr int x = decltype(xc)::value, e = decltype(ec)::value, b = decltype(bc)::value;
+      pe_t[b][e % EPM] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x][e], p.c, -L[(e >> 2) & 1][e & 3]));
+      sd_t[b][e % EPM] = dp[x][e] - Dv[(e >> 2) & 1][e & 3];
+    };
+    auto back = [&](auto xc, auto ec, auto bc) {
+      constexpr int x = decltype(xc)::value, e = decltype(ec)::value, b = decltype(bc)::value;
+      const float pe = pe_t[b][e % EPM];
       pb[x][e >> 3][e & 7] = (__bf16)pe;
-      dsb[x][e >> 3][e & 7] = (__bf16)ds;
+      dsb[x][e >> 3][e & 7] = (__bf16)(pe * sd_t[b][e % EPM]);
     };
     auto step = [&](auto fc) {
       constexpr int f = decltype(fc)::value, grp = f / NG, i = f % NG;
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
         if constexpr (i & 1)
           dp[grp] = mfma(fr[f % RING], vf[kk], kk == 0 ? f32x16{} : dp[grp]);
         else
-          s[grp] = mfma(fr[f % RING], kf[kk], kk == 0 ? sinit[grp] : s[grp]);
+          s[grp] = mfma(fr[f % RING], kf[kk], kk == 0 ? (MASKED ? sinit[grp] : f32x16{}) : s[grp]);
       } else {
         constexpr int x = grp - 2, st = i / (NG / 2), db = (i % (NG / 2)) >> 1;
         if constexpr (i & 1)
@@ -281,7 +295,17 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
       if constexpr (grp == 1 || grp == 2) {
         [&]<int... E>(std::integer_sequence<int, E...>) {
-          (elem(std::integral_constant<int, grp - 1>{}, std::integral_constant<int, EPM * i + E>{}), ...);
+          (front(std::integral_constant<int, grp - 1>{}, std::integral_constant<int, EPM * i + E>{},
+                 std::integral_constant<int, i & 1>{}), ...);
+          if constexpr (i > 0)
+            (back(std::integral_constant<int, grp - 1>{}, std::integral_constant<int, EPM * (i - 1) + E>{},
+                  std::integral_constant<int, (i - 1) & 1>{}), ...);
+        }(std::make_integer_sequence<int, EPM>{});
+      }
+      if constexpr ((grp == 2 || grp == 3) && i == 0) {
+        [&]<int... E>(std::integer_sequence<int, E...>) {
+          (back(std::integral_constant<int, grp - 2>{}, std::integral_constant<int, EPM * (NG - 1) + E>{},
+                std::integral_constant<int, (NG - 1) & 1>{}), ...);
         }(std::make_integer_sequence<int, EPM>{});
       }
     };
@@ -293,8 +317,11 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     }(std::make_integer_sequence<int, NF>{});
   };
 
-  if (t0 < t1) issue(t0, stage(0));
-  for (int t = t0; t < t1; ++t) {
+  // Tiles before tm hold a query that misses a key of this workgroup (causal): they take
+  // the masked stream; from tm on every pair is visible and the stream has no mask.
+  const int tm = CAUSAL ? min(t1, max(t0, (k0 + kBwdKeyRows - 1 - p.off + kRows - 1) / kRows)) : t0;
+  auto body = [&](int t, auto maskedc) {
+    constexpr bool MASKED = decltype(maskedc)::value;
     const int cur = (t - t0) & 1;
     wait_loads();  // tile t (the only loads in flight)
     wg_barrier();  // tile t visible to all; everyone is done with the other stage
@@ -303,14 +330,14 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     const char* dOs = Qs + C::TILEB;
     const float* sts = (const float*)(Qs + 2 * C::TILEB);
     const int qa0 = t * kRows;
-    // no query of this tile sees a key of this wave (causal): nothing to add
-    if (CAUSAL && qa0 + kRows - 1 + p.off < kw0) continue;
-    // Masked pairs enter as S = -inf through the initial accumulator of the S product, so
-    // that P = exp2(-inf) = 0 and dS = 0 with no extra work in the stream; element e of
-    // step x is query qa0 + 32x + 8(e/4) + 4g + e%4 and is masked iff key > query + off.
-    // Query rows past Nq need no mask: their LSE2 is +inf.
     f32x16 sinit[2] = {f32x16{}, f32x16{}};
-    if (CAUSAL && qa0 + p.off < kw0 + 31) {  // the tile's first query misses a key
+    if constexpr (MASKED) {
+      // no query of this tile sees a key of this wave: nothing to add
+      if (qa0 + kRows - 1 + p.off < kw0) return;
+      // Masked pairs enter as S = -inf through the initial accumulator of the S product, so
+      // that P = exp2(-inf) = 0 and dS = 0 with no extra work in the stream; element e of
+      // step x is query qa0 + 32x + 8(e/4) + 4g + e%4 and is masked iff key > query + off.
+      // Query rows past Nq need no mask: their LSE2 is +inf.
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int lim = key - p.off - qa0 - 32 * x - 4 * g;  // visible iff 8(e/4) + e%4 >= lim
@@ -318,7 +345,28 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) sinit[x][e] = (8 * (e >> 2) + (e & 3) < lim) ? -INFINITY : 0.f;
       }
     }
-    tile_stream(Qs, dOs, sts, sinit);
+    tile_stream(maskedc, Qs, dOs, sts, sinit);
+  };
+  auto pin = [](f32x16 (&a)[D / 32], f32x16 (&b)[D / 32]) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(a[db]), "+a"(b[db]));
+  };
+
+  if (t0 < t1) issue(t0, stage(0));
+  // The K and V rows must have landed before the loop, and the compiler must not wait for
+  // them inside it: its own vmcnt count ignores the direct loads issued there, so a wait it
+  // placed before the first use of kf/vf would also wait for the next tile's loads.
+  wait_loads();
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
+  int t = t0;
+  for (; t < tm; ++t) {
+    body(t, std::true_type{});
+    pin(dk, dv);
+  }
+  for (; t < t1; ++t) {
+    body(t, std::false_type{});
+    pin(dk, dv);
   }
 
   // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4.
