@@ -18,8 +18,10 @@
 //      32 keys' K and V rows in VGPRs and their dK, dV in float32 accumulators while the
 //      query tiles (Q, dO and the row statistics, 64 rows each) stream through LDS. Each
 //      tile is one stream of MFMAs with the fragment reads prefetched and the float32 work
-//      of one 32-query step spread between the MFMAs of the other step; masked pairs enter
-//      as S = -inf through the initial accumulator, so every tile runs the same code.
+//      of one 32-query step spread between the MFMAs of the other step. On the few tiles
+//      that cross the causal diagonal, masked pairs enter as S = -inf through the initial
+//      accumulator of the S product (same stream, its own loop); the other tiles start it
+//      from zero.
 //   3. bwd_dq_kernel: one workgroup per 128 query rows of one (b, h); each wave keeps 32
 //      rows' Q and dO in VGPRs and its dQ in float32 accumulators while 64-key K and V tiles
 //      stream through LDS. It recomputes S and dP rather than adding partial dQ from the
