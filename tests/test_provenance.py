@@ -12,7 +12,7 @@ def test_comments_and_layout_do_not_change_the_code_text():
 def test_a_code_change_changes_the_code_text():
     a = "int f(int x) { return x + 1; }"
     assert P.code_text(a) != P.code_text(a.replace("+ 1", "+ 2"))
-    assert P.code_text(a) != P.code_text(a.replace("x + 1", "x+1").replace("int f", "intf"))
+    assert P.code_text(a) != P.code_text(a.replace("int f", "intf"))
 
 
 def test_every_kind_hashes_its_sources():
