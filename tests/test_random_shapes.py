@@ -161,3 +161,31 @@ def test_random_backward(dtype):
         torch.cuda.synchronize()
         st = _all_rows(q, k, v, do, scale, causal, dq, dk, dv, what, **bounds)
         say(f"  {st}")
+
+
+def test_random_fp8():
+    """E4M3 inputs with per-tensor descales, at the FP8 bounds of the FP8 parity tests."""
+    from test_fp8_parity import _case as fp8_case
+    rng = np.random.default_rng(7051)
+    for c in range(8):
+        B, H, nq, nk, _, causal, _, mult = _case(rng, 1_000_000)
+        say(f"fp8 case {c}: B={B} H={H} Nq={nq} Nk={nk} causal={causal} mult={mult:.2f}")
+        st = fp8_case(B, H, nq, nk, causal, 9500 + c, mult=mult)
+        say(f"  {st}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_random_paged(dtype):
+    """Random page sizes, per-sequence lengths (zero included) and chunk counts over a pool
+    with pages in random order."""
+    from test_paged_parity import _case as paged_case
+    rng = np.random.default_rng(7061 if dtype == torch.bfloat16 else 7062)
+    for c in range(8):
+        d = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 6)), int(rng.integers(1, 5))
+        ps = int(rng.choice([1, 4, 16, 64, 128, 256]))
+        lens = [0 if rng.random() < 0.1 else _len(rng, 1, 6000 if ps > 1 else 300)
+                for _ in range(B)]
+        S = int(rng.integers(1, 100))
+        st = paged_case(B, H, d, ps, lens, S, dtype, 9600 + 10 * c)
+        say(f"  {st}")
