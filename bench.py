@@ -243,7 +243,8 @@ def fp8_record(num: int, steps: int, warmup: int):
     wall_ms, ev_ms = time_launches(step, steps, warmup)
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     rec = {
-        "workload": f"{w.name}, inputs E4M3 (per-tensor descale max|x|/448)",
+        "workload": f"{w.name.replace('bf16 ', 'E4M3 ', 1)} (the same float32 draws quantised per "
+                    f"tensor, descale max|x|/448)",
         "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
         "flops_per_launch": w.flops, "ms_per_step": wall_ms, "kernel_ms": ev_ms,
         "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
