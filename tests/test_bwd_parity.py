@@ -117,6 +117,25 @@ def test_bwd_many_heads_grid_mapping(d):
             _all_rows(q, k, v, do, finite_scale(d), causal, dq, dk, dv, f"B={B} H={H}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [1, 2], ids=["bottom_right", "top_left"])
+def test_bwd_diagonal_loop_boundaries(d, causal):
+    """The dK/dV kernel runs the query tiles that cross the causal diagonal in a loop of their
+    own before the unmasked ones; these shapes put the switch at even and odd tile counts,
+    at the first tile (keys offset far behind the queries) and past the last one (keys far
+    ahead), with several 128-key workgroups per head."""
+    for nq, nk in [(1000, 1000), (1000, 1064), (1064, 1000), (640, 2000), (2000, 640),
+                   (130, 1500), (1500, 130)]:
+        say(f"bwd diagonal loops d={d} causal={causal} Nq={nq} Nk={nk}")
+        q = seeded((1, 2, nq, d), 31, torch.bfloat16, mult=2.0)
+        k = seeded((1, 2, nk, d), 32, torch.bfloat16, mult=2.0)
+        v = seeded((1, 2, nk, d), 33, torch.bfloat16)
+        do = seeded((1, 2, nq, d), 34, torch.bfloat16)
+        dq, dk, dv = _fwd_bwd(q, k, v, do, finite_scale(d), causal)
+        st = _all_rows(q, k, v, do, finite_scale(d), causal, dq, dk, dv, f"Nq={nq} Nk={nk}")
+        say(f"  {st}")
+
+
 # ------------------------------------------------------------------ named workloads
 
 def _sampled_workload(num, heads_kv, per_head_q, per_head_k):
