@@ -121,13 +121,21 @@ __global__ __launch_bounds__(kT, 1) void bwd_f32_dkdv_kernel(BwdParams p) {
     vr[st] = key < p.Nk ? vh[(size_t)key * D + 2 * st + g] : 0.f;
   }
   f32x16 dk[NDB], dv[NDB];
+  // The accumulators stay in the matrix registers (AGPRs) for the whole loop: the empty asm
+  // here and at the top of every iteration keeps the compiler from parking them in VGPRs
+  // at the loop edge and copying them across every tile.
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = dv[db] = f32x16{};
+    asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+  }
 
   // queries that can see one of this workgroup's keys: i + off >= k0 when causal
   int q_first = 0;
   if (CAUSAL) q_first = max(0, k0 - p.off) / kTile * kTile;
   for (int q0 = q_first; q0 < p.Nq; q0 += kTile) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
     __syncthreads();  // the previous tile has been read
     stage_rows<D, PITCH>(Qs, qh, q0, p.Nq, tid);
     stage_rows<D, PITCH>(Ds, doh, q0, p.Nq, tid);
@@ -218,7 +226,10 @@ __global__ __launch_bounds__(kT, 1) void bwd_f32_dq_kernel(BwdParams p) {
   const float dsm = ws_dsum(p, bh)[qrow];
   f32x16 dq[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) {
+    dq[db] = f32x16{};
+    asm volatile("" : "+a"(dq[db]));  // kept in AGPRs across the loop, as in the dK/dV kernel
+  }
 
   int kv_end = p.Nk;
   int wave_kv_end = wq0 < p.Nq ? p.Nk : 0;
@@ -227,6 +238,8 @@ __global__ __launch_bounds__(kT, 1) void bwd_f32_dq_kernel(BwdParams p) {
     if (wq0 < p.Nq) wave_kv_end = min(p.Nk, min(wq0 + 31, p.Nq - 1) + p.off + 1);
   }
   for (int k0 = 0; k0 < kv_end; k0 += kTile) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(dq[db]));
     __syncthreads();
     stage_rows<D, PITCH>(Ks, kh, k0, p.Nk, tid);
     stage_rows<D, PITCH>(Vs, vh, k0, p.Nk, tid);
