@@ -185,7 +185,8 @@ def prefill_record(num: int, steps: int, warmup: int):
         "ms_per_step": wall_ms, "kernel_ms": ev_ms,
         "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_for("fwd_bf16", num)},
+                     "frac": achieved / peak,
+                     "traffic": traffic_for("fwd_bf16" if w.dtype == torch.bfloat16 else "fwd_f32", num)},
     }
     return rec, (w, q, k, v)
 
@@ -495,6 +496,13 @@ def main():
         rec4, _ = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
         rec4.pop("step")
         extra["prefill_N30000"] = rec4
+        torch.cuda.empty_cache()
+        # the two smaller shapes: bf16 d=64 non-causal, and the float32 instance (a few
+        # workgroups: launch-latency bound, reported for completeness)
+        for key, num in (("prefill_N2048_d64", 2), ("prefill_f32_N256_d64", 1)):
+            rec, _ = prefill_record(num, max(5, args.steps // 2), max(2, args.warmup // 2))
+            rec.pop("step")
+            extra[key] = rec
         torch.cuda.empty_cache()
         extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["prefill_fp8_N30000"] = fp8_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
