@@ -10,8 +10,11 @@ are timed after it and reported in the same JSON line under "also".
 
 Prints ONE JSON line. `roofline.achieved` is the algorithmic FLOPs (4*B*H*Nq*Nk*d,
 halved for causal) of one launch divided by the kernel's average duration from HIP
-events on the launch stream; `cpu_baseline` times the float64 oracle on a bounded row
-sample of the same workload on this host's cores.
+events on the launch stream. Every leg first warms up untimed for a few seconds (the
+shader clock needs that long to settle). `cpu_baseline` times the float64 oracle on this
+host's cores beside each workload leg: every row of the small workloads (N=256 float32,
+N=2048 d=64, the decode), a bounded row sample of the two large causal prefills with the
+whole workload's time extrapolated from it.
 """
 from __future__ import annotations
 
@@ -56,18 +59,38 @@ def bwd_traffic(workload: int):
 
 
 LAST_REPS = {}  # per-block event times of the latest time_launches call
+LAST_WARMUP = {}  # untimed warm-up of the latest time_launches call (launches, seconds)
 
 
-def time_launches(fn, steps: int, warmup: int, blocks: int = 5):
+WARMUP_SECONDS = 2.0  # untimed warm-up of each leg after its `warmup` steps (see time_launches)
+
+
+def time_launches(fn, steps: int, warmup: int, blocks: int = 5, warmup_s: float | None = None):
     """(wall ms per step, event ms per launch). fn launches on torch's current stream.
+
+    Warm-up, all outside the timed region: `warmup` calls, then more calls until at least
+    `warmup_s` seconds (default WARMUP_SECONDS) have passed since the first one. A handful of
+    launches lasts a few milliseconds, too short for the shader clock to settle under the
+    new load (blocks of 4 launches timed right after 5 warm-up ones ran 0.67 ms falling to
+    0.57 ms), so the timed steps would mix two clock states.
 
     Events are also recorded between `blocks` equal blocks of the timed steps (on the same
     stream, with no synchronisation inside the timed region); the per-launch time of each
     block goes to LAST_REPS["block_ms"] and their median to LAST_REPS["median_ms"]."""
     import torch
+    warmup_s = WARMUP_SECONDS if warmup_s is None else warmup_s
+    t_w = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - t_w < warmup_s:
+        for _ in range(10):
+            fn()
+        extra += 10
+        torch.cuda.synchronize()
+    LAST_WARMUP.clear()
+    LAST_WARMUP.update({"steps": warmup + extra, "seconds": time.perf_counter() - t_w})
     nb = max(1, min(blocks, steps))
     edges = [round(i * steps / nb) for i in range(nb + 1)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
@@ -128,41 +151,66 @@ def clock_under_load(step, seconds: float = 2.0):
                       "while the headline prefill ran back to back (outside the timed steps)"}
 
 
-def cpu_baseline(w, q, k, v, target_s: float):
-    """Time the oracle on a row sample sized for about target_s seconds; report the
-    algorithmic rate (same FLOP convention as the GPU figure)."""
+def visible_keys(w, rows):
+    """Visible keys of each flat query row (b*H + h)*Nq + i of workload w (mask included)."""
+    import numpy as np
+    i = np.asarray(rows, dtype=np.int64) % w.Nq
+    if w.causal:
+        return np.clip(i + (w.Nk - w.Nq) + 1, 0, w.Nk)
+    return np.full(i.shape, w.Nk, dtype=np.int64)
+
+
+def cpu_baseline(w, q, k, v, target_s: float, full: bool = False):
+    """Time the float64 oracle, unmodified, on this host's cores over the same workload and
+    report its algorithmic rate (the GPU figure's FLOP or byte convention).
+
+    full: every query row of the workload. Otherwise a uniform random sample of rows sized
+    for about target_s seconds (a 256-row probe sets the size), reported with the time the
+    whole workload would take at the sample's rate (time scales with the visible keys)."""
     import numpy as np
     import oracle
+    t_copy = time.perf_counter()
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    copy_s = time.perf_counter() - t_copy
     threads = oracle.default_threads()
     total_rows = w.B * w.H * w.Nq
 
     def row_flops(rows):
-        i = np.asarray(rows) % w.Nq
-        keys = np.minimum(w.Nk, i + (w.Nk - w.Nq) + 1) if w.causal else np.full(i.shape, w.Nk)
-        return float(4.0 * w.d * keys.sum())
+        return float(4.0 * w.d * visible_keys(w, rows).sum())
 
     rng = np.random.default_rng(0)
-    probe = np.sort(rng.choice(total_rows, size=min(total_rows, 256), replace=False))
-    t0 = time.perf_counter()
-    oracle.attention(qc, kc, vc, w.scale, w.causal, rows=probe, threads=threads)
-    rate = row_flops(probe) / max(1e-6, time.perf_counter() - t0)
-    per_row = row_flops(probe) / len(probe)
-    n = int(min(total_rows, max(256, target_s * rate / per_row)))
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    if full:
+        rows, n = None, total_rows
+    else:
+        probe = np.sort(rng.choice(total_rows, size=min(total_rows, 256), replace=False))
+        t0 = time.perf_counter()
+        oracle.attention(qc, kc, vc, w.scale, w.causal, rows=probe, threads=threads)
+        rate = row_flops(probe) / max(1e-6, time.perf_counter() - t0)
+        per_row = row_flops(probe) / len(probe)
+        n = int(min(total_rows, max(256, target_s * rate / per_row)))
+        rows = np.sort(rng.choice(total_rows, size=n, replace=False))
     t0 = time.perf_counter()
     oracle.attention(qc, kc, vc, w.scale, w.causal, rows=rows, threads=threads)
     sec = time.perf_counter() - t0
-    flops = row_flops(rows)
-    # the whole workload at the sample's rate: time scales with the visible keys of the rows
-    full_s = sec * row_flops(np.arange(total_rows)) / flops
-    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {total_rows} query rows (uniform random, seed 0) of the same "
-                      f"workload, all their visible keys; {flops / 1e9:.1f} GFLOP in {sec:.1f} s",
-            "extrapolated_full_workload_s": full_s}
+    flops = row_flops(np.arange(total_rows) if rows is None else rows)
+    rec = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "seconds": sec, "host_copy_s": copy_s}
+    if full:
+        rec["sample"] = (f"full workload: all {total_rows} query rows, all their visible keys; "
+                         f"{flops / 1e9:.2f} GFLOP in {sec:.2f} s")
+    else:
+        full_s = sec * row_flops(np.arange(total_rows)) / flops
+        rec["sample"] = (f"{n} of {total_rows} query rows (uniform random, seed 0) of the same "
+                         f"workload, all their visible keys; {flops / 1e9:.1f} GFLOP in {sec:.1f} s")
+        rec["extrapolated_full_workload_s"] = full_s
+        rec["extrapolation"] = ("the sample's time scaled by the visible keys of all rows over "
+                                "those of the sampled rows")
+    if w.num_splits:  # decode: the same figure in the GPU leg's unit
+        rec["value_gbps"] = w.io_bytes / sec / 1e9
+    return rec
 
 
-def prefill_record(num: int, steps: int, warmup: int):
+def prefill_record(num: int, steps: int, warmup: int, warmup_s: float | None = None):
     import torch
     import exact_tiled_attention_08_amd as fa
     import workloads as W
@@ -174,12 +222,12 @@ def prefill_record(num: int, steps: int, warmup: int):
     def step():
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
-    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    wall_ms, ev_ms = time_launches(step, steps, warmup, warmup_s=warmup_s)
     reps = dict(LAST_REPS)
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
     rec = {"step": step, "kernel_ms_blocks": reps["block_ms"],
-           "kernel_ms_median_of_blocks": reps["median_ms"],
+           "kernel_ms_median_of_blocks": reps["median_ms"], "warmup_untimed": dict(LAST_WARMUP),
         "workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
         "causal": w.causal, "flops_per_launch": w.flops,
         "ms_per_step": wall_ms, "kernel_ms": ev_ms,
@@ -325,7 +373,9 @@ def bwd_record(num: int, steps: int, warmup: int):
     return rec
 
 
-def decode_record(steps: int, warmup: int):
+def decode_record(steps: int, warmup: int, cpu: bool = False):
+    """fa_decode_splitkv on the decode workload; with cpu, also the oracle over every
+    (b, h) of the same cache on the host's cores (cpu_baseline, full)."""
     import torch
     import exact_tiled_attention_08_amd as fa
     import workloads as W
@@ -347,7 +397,10 @@ def decode_record(steps: int, warmup: int):
         "note": "kernel_ms spans both launches of one call (split + merge)",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for("decode", 5)},
+        "warmup_untimed": dict(LAST_WARMUP),
     }
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, 0.0, full=True)
     del q, k, v
     torch.cuda.empty_cache()
     return rec
@@ -482,33 +535,46 @@ def main():
         "kernel_ms": main_rec["kernel_ms"],
         "kernel_ms_median_of_blocks": main_rec["kernel_ms_median_of_blocks"],
         "kernel_ms_blocks": main_rec["kernel_ms_blocks"],
+        "warmup_untimed": main_rec["warmup_untimed"],
         "mfma_probe": {"tflops": probe_tf, "frac_of_peak": probe_tf / PEAK_BF16_TFLOPS,
                        "what": "fa_probe_mfma: back-to-back bf16 32x32x16 MFMAs on register "
                                "operands, no memory traffic, 2048 workgroups x 4 waves"},
         "clock": clock,
     }
-    if args.only is None and not args.no_cpu:
+    cpu = args.only is None and not args.no_cpu
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     del q, k, v
     torch.cuda.empty_cache()
     if args.only is None and not args.no_extra:
         extra = {}
-        rec4, _ = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
+        # the legs after the headline run back to back: a shorter untimed warm-up each
+        leg_w = 1.0
+        rec4, (w4, q4, k4, v4) = prefill_record(4, max(3, args.steps // 5), max(1, args.warmup // 5),
+                                                warmup_s=leg_w)
         rec4.pop("step")
+        if cpu:  # sampled rows, extrapolated to the whole workload
+            rec4["cpu_baseline"] = cpu_baseline(w4, q4, k4, v4, args.cpu_seconds)
         extra["prefill_N30000"] = rec4
+        del q4, k4, v4
         torch.cuda.empty_cache()
         # the two smaller shapes: bf16 d=64 non-causal, and the float32 instance (a few
-        # workgroups: launch-latency bound, reported for completeness)
+        # workgroups: launch-latency bound, reported for completeness); the oracle runs
+        # every row of both
         for key, num in (("prefill_N2048_d64", 2), ("prefill_f32_N256_d64", 1)):
-            rec, _ = prefill_record(num, max(5, args.steps // 2), max(2, args.warmup // 2))
+            rec, (wx, qx, kx, vx) = prefill_record(num, max(5, args.steps // 2),
+                                                   max(2, args.warmup // 2), warmup_s=leg_w)
             rec.pop("step")
+            if cpu:
+                rec["cpu_baseline"] = cpu_baseline(wx, qx, kx, vx, 0.0, full=True)
             extra[key] = rec
+            del qx, kx, vx
         torch.cuda.empty_cache()
         extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["prefill_fp8_N30000"] = fp8_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
         extra["prefill_bias"] = bias_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["prefill_varlen"] = varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
-        extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup))
+        extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup), cpu=cpu)
         extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))
         extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         out["also"] = extra

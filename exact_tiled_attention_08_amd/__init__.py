@@ -166,6 +166,40 @@ def _check_inputs(q, k, v):
         raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
 
 
+def _out_arg(t, shape, device, name: str, dtype=None):
+    """A caller's output tensor checked against what the kernels write (a new one if t is
+    None): a contiguous tensor of exactly `shape` and `dtype` (float32 by default) on
+    `device`. The C ABI takes bare device pointers and cannot size them, so a host tensor, a
+    short buffer or one on another GPU must be refused here, before any launch."""
+    import torch
+    dtype = torch.float32 if dtype is None else dtype
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)}, "
+                         f"got {t.dtype} {list(t.shape)}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    return t
+
+
+def _workspace_arg(t, need: int, device):
+    """A caller's workspace checked for device and size in bytes (a new one if t is None)."""
+    import torch
+    if t is None:
+        return torch.empty((max(int(need), 16),), dtype=torch.uint8, device=device)
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"workspace must be a GPU tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < need:
+        raise ValueError(f"workspace holds {have} bytes, {need} needed")
+    return t
+
+
 def _causal_arg(causal) -> int:
     """False/0: no mask; True/1: causal, queries at the end of the key sequence (bottom-right);
     2: causal, queries at its start (top-left)."""
@@ -189,15 +223,9 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
     Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
-    elif out.shape != (B, H, Nq, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, H, Nq, d] tensor")
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32
-                              or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    out = _out_arg(out, (B, H, Nq, d), q.device, "out")
+    if return_lse or lse is not None:
+        lse = _out_arg(lse, (B, H, Nq), q.device, "lse")
     st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr() if lse is not None else None,
                           B, H, Nq, Nk, d, float(scale), _causal_arg(causal), _dtype_code(q),
@@ -255,15 +283,9 @@ def fwd_bias(q, k, v, bias, scale: float | None = None, causal: bool = False, ou
     be, sb, sh, sq = _bias_strides(bias, q, B, H, Nq, Nk)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
-    elif out.shape != (B, H, Nq, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, H, Nq, d] tensor")
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32
-                              or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    out = _out_arg(out, (B, H, Nq, d), q.device, "out")
+    if return_lse or lse is not None:
+        lse = _out_arg(lse, (B, H, Nq), q.device, "lse")
     st = library().fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), be.data_ptr(), sb, sh, sq,
                                out.data_ptr(), lse.data_ptr() if lse is not None else None,
                                B, H, Nq, Nk, d, float(scale), _causal_arg(causal), _dtype_code(q),
@@ -288,10 +310,10 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
         raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    out = _out_arg(out, (B, H, Nq, d), q.device, "out")
+    lse = _out_arg(lse, (B, H, Nq), q.device, "lse")
     st = library().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                               B, H, Nq, Nk, d, float(scale), float(q_descale), float(k_descale),
                               float(v_descale), _causal_arg(causal), _stream_ptr(q.device))
@@ -321,10 +343,10 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: fl
     B = cu_seqlens_q.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((total_q, H, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if len({t.device for t in (q, k, v, cu_seqlens_q, cu_seqlens_k)}) != 1:
+        raise ValueError("q, k, v and the sequence offsets must be on one device")
+    out = _out_arg(out, (total_q, H, d), q.device, "out")
+    lse = _out_arg(lse, (H, total_q), q.device, "lse")
     st = library().fa_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k,
@@ -345,13 +367,11 @@ def decode(q, k, v, num_splits: int = 64, scale: float | None = None, out=None, 
     Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, H, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, H, 1, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    if int(num_splits) < 1:
+        raise ValueError("num_splits must be at least 1")
+    workspace = _workspace_arg(workspace, decode_workspace_bytes(B, H, d, num_splits), q.device)
+    out = _out_arg(out, (B, H, 1, d), q.device, "out")
+    lse = _out_arg(lse, (B, H, 1), q.device, "lse")
     st = library().fa_decode_splitkv(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, H, Nk, d, float(scale), int(num_splits), workspace.data_ptr(),
@@ -382,16 +402,16 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits: int = 6
         raise ValueError("block_table must be int32 [B, max_pages]")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
+    if len({t.device for t in (q, k_cache, v_cache, block_table, seq_lens)}) != 1:
+        raise ValueError("q, the caches, block_table and seq_lens must be on one device")
     num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, H, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, H, 1, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    if int(num_splits) < 1:
+        raise ValueError("num_splits must be at least 1")
+    workspace = _workspace_arg(workspace, decode_workspace_bytes(B, H, d, num_splits), q.device)
+    out = _out_arg(out, (B, H, 1, d), q.device, "out")
+    lse = _out_arg(lse, (B, H, 1), q.device, "lse")
     st = library().fa_decode_paged(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
         seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, d, page_size, num_pages,
@@ -421,19 +441,10 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, d
     if scale is None:
         scale = 1.0 / math.sqrt(d)
 
-    def out(t, shape):
-        if t is None:
-            return torch.empty(shape, dtype=torch.float32, device=q.device)
-        if t.shape != shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"gradient outputs must be contiguous float32 {shape} tensors")
-        return t
-
-    dq = out(dq, (B, H, Nq, d))
-    dk = out(dk, (B, H, Nk, d))
-    dv = out(dv, (B, H, Nk, d))
-    need = bwd_workspace_bytes(B, H, Nq)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    dq = _out_arg(dq, (B, H, Nq, d), q.device, "dq")
+    dk = _out_arg(dk, (B, H, Nk, d), q.device, "dk")
+    dv = _out_arg(dv, (B, H, Nk, d), q.device, "dv")
+    workspace = _workspace_arg(workspace, bwd_workspace_bytes(B, H, Nq), q.device)
     st = library().fa_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d, float(scale),

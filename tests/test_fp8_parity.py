@@ -4,12 +4,14 @@ dequantized inputs (E4M3 value * descale).
 Tolerance (derived from the arithmetic; the stated bounds cover bfloat16 and float32): the
 scores are float32 sums of exact products; each weight enters the second product as
 E4M3(256 p), whose relative rounding error is at most 2^-4 (three mantissa bits), while the
-normaliser sums the float32 weights. So every output element is off by at most
-2^-4 * sum_j p_j |v_j| <= 2^-4 * max|V| (plus float32 rounding; weights below 2^-18 of the
-row max, which E4M3 cannot hold, carry negligible mass). A float32 model of this arithmetic
-stays within 0.07 (max) and 0.004 (mean) on N = 512..4096 with and without the causal mask
-and with the sharp x3 inputs. Bounds:
-    max|O - O*| <= 2^-4 * max|V|,   mean|O - O*| <= 1e-2,   max|LSE - LSE*| <= 1e-3.
+normaliser sums the float32 weights, so an output element is off by at most
+2^-4 * sum_j p_j |v_j| <= 2^-4 * max|V| in the worst case (weights below 2^-18 of the row
+max, which E4M3 cannot hold, carry negligible mass). Typical errors are far smaller: a
+float32 model of this arithmetic (tests/tolerance_model.py, checked by
+tests/test_tolerance_model.py) stays within 0.070 (max) and 0.0039 (mean) on N = 300..4096
+with and without the causal mask, with Q, K scaled x1 to x3 and V drawn N(0,1) as in every
+case here. Bounds, about 1.7x (max) and 1.5x (mean) that:
+    max|O - O*| <= 0.12,   mean|O - O*| <= 6e-3,   max|LSE - LSE*| <= 1e-3.
 """
 import math
 
@@ -20,12 +22,12 @@ import torch
 import exact_tiled_attention_08_amd as fa
 import oracle
 import workloads as W
-from parity_util import rows_of, say
+from parity_util import FP8_LSE_MAX, FP8_O_MAX, FP8_O_MEAN, rows_of, say
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-FP8_MEAN, FP8_LSE = 1e-2, 1e-3
+FP8_MEAN, FP8_LSE = FP8_O_MEAN, FP8_LSE_MAX
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -49,7 +51,9 @@ def compare_fp8(o, lse, o_ref, l_ref, vmax, what):
     err = np.abs(o - o_ref)
     lerr = np.abs(lse[~empty] - l_ref[~empty]) if np.any(~empty) else np.zeros(1)
     st = dict(o_max=float(err.max()), o_mean=float(err.mean()), lse_max=float(lerr.max()),
-              bound=2.0 ** -4 * vmax)
+              bound=FP8_O_MAX)
+    # the worst case of the arithmetic holds whatever the values
+    assert st["o_max"] <= 2.0 ** -4 * vmax, f"{what}: O max err beyond the worst case"
     assert st["o_max"] <= st["bound"], f"{what}: O max err {st['o_max']:.3e} > {st['bound']:.3e}"
     assert st["o_mean"] <= FP8_MEAN, f"{what}: O mean err {st['o_mean']:.3e}"
     assert st["lse_max"] <= FP8_LSE, f"{what}: LSE max err {st['lse_max']:.3e}"

@@ -48,7 +48,7 @@ def test_workload_full(num):
     say(f"  {st}")
 
 
-@pytest.mark.parametrize("num,per_head", [(3, 64), (4, 32)])
+@pytest.mark.parametrize("num,per_head", [(3, 64), (4, 64)])
 def test_workload_sampled(num, per_head):
     w = W.WORKLOADS[num]
     say(f"workload {num}: {w.name} (sampled rows, {per_head} per head)")
