@@ -10,6 +10,7 @@ not on the GPU, the call raises.
     o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)  # packed batch
     o, lse = fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale)   # E4M3 inputs
     o, lse = decode(q, k, v, num_splits=64, scale=None)     # one query per (b, h)
+    o, lse = decode_noalloc(q, k, v, num_splits=64)         # the same, no device allocation
     o, lse = decode_paged(q, k_cache, v_cache, block_table, seq_lens)  # paged cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, scale=None, causal=False)   # gradients
 
@@ -22,7 +23,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_bias", "pad_bias", "fwd_fp8", "fwd_varlen", "decode", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str",
+__all__ = ["fwd", "fwd_bias", "pad_bias", "fwd_fp8", "fwd_varlen", "decode", "decode_noalloc", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str", "NOALLOC_SCRATCH_BYTES",
            "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
@@ -32,9 +33,12 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_VALUE, FA_ERR_ALIGN = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
+# FA_NOALLOC_SCRATCH_BYTES of include/fa.h: the fixed per-GPU scratch of fa_decode_splitkv_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_bias", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_paged",
+EXPORTS = ("fa_fwd", "fa_fwd_bias", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+           "fa_decode_splitkv_noalloc", "fa_decode_paged",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_probe_mfma", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
@@ -48,6 +52,7 @@ _SIGS = {
                            _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
+    "fa_decode_splitkv_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
                              _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
@@ -377,6 +382,29 @@ def decode(q, k, v, num_splits: int = 64, scale: float | None = None, out=None, 
         B, H, Nk, d, float(scale), int(num_splits), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _dtype_code(q), _stream_ptr(q.device))
     _raise(st, "fa_decode_splitkv")
+    return out, lse
+
+
+def decode_noalloc(q, k, v, num_splits: int = 64, scale: float | None = None, out=None,
+                   lse=None):
+    """decode() through fa_decode_splitkv_noalloc: the partial states live in the library's
+    fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES), so the C call allocates nothing. Pass
+    out and lse to allocate nothing here either (torch allocates them if they are None).
+    Calls that overlap in time on one GPU share that scratch and must not be issued."""
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    if Nq != 1:
+        raise ValueError("decode takes exactly one query per (b, h): q must be [B, H, 1, d]")
+    if int(num_splits) < 1:
+        raise ValueError("num_splits must be at least 1")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out_arg(out, (B, H, 1, d), q.device, "out")
+    lse = _out_arg(lse, (B, H, 1), q.device, "lse")
+    st = library().fa_decode_splitkv_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+        k.shape[2], d, float(scale), int(num_splits), _dtype_code(q), _stream_ptr(q.device))
+    _raise(st, "fa_decode_splitkv_noalloc")
     return out, lse
 
 

@@ -277,6 +277,24 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
   return finish_launch(e);
 }
 
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, float* o,
+                                    float* lse, int B, int H, int Nk, int d, float scale,
+                                    int num_splits, fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nk < 1 || d < 1 || num_splits < 1) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+  if (need == 0 || need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  // the device the work runs on: the stream's (the current one for the null stream)
+  int device = -1;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return finish_launch(e);
+  void* ws = nullptr;
+  if ((e = fa::decode_scratch(device, &ws)) != hipSuccess) return finish_launch(e);
+  return fa_decode_splitkv(q, k, v, o, lse, B, H, Nk, d, scale, num_splits, ws,
+                           (size_t)FA_NOALLOC_SCRATCH_BYTES, dtype, stream);
+}
+
 fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                           const int* block_table, const int* seq_lens, float* o, float* lse,
                           int B, int H, int d, int page_size, int num_pages, int max_pages_per_seq,

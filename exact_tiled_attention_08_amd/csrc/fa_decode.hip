@@ -26,9 +26,51 @@
 // keys, then loads the key's row from that page; a page id outside the pool is never read
 // through and its keys are skipped. Sequence lengths may differ: each sequence's keys are
 // split into S chunks of its own.
+#include <mutex>
+
+#include "../../include/fa.h"
+
 #include "fa_internal.h"
 
+// Partial states of the allocation-free decode entry point (fa_decode_splitkv_noalloc): a
+// fixed device array in place of a caller's workspace, for callers that cannot allocate
+// device memory. Every GPU the library runs on holds its own copy until the process ends.
+// Host code never passes this name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
 namespace fa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+}  // namespace
+
+hipError_t decode_scratch(int device, void** ptr) {
+  *ptr = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    // once per device, with that device current
+    int current = -1;
+    hipError_t e = hipGetDevice(&current);
+    if (e != hipSuccess) return e;
+    if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (current != device) {
+      const hipError_t back = hipSetDevice(current);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (!addr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = addr;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kNT = 256;  // threads per split workgroup

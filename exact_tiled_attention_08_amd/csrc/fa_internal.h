@@ -161,6 +161,9 @@ int fwd_fp8_block_rows();
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s);
+// Device address of the decode's fixed scratch array on `device` (looked up once per device
+// with hipGetSymbolAddress, then cached); FA_NOALLOC_SCRATCH_BYTES long.
+hipError_t decode_scratch(int device, void** ptr);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int d, bool causal, hipStream_t s);
 

@@ -169,6 +169,28 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
                             void* stream);
 
 /*
+ * fa_decode_splitkv_noalloc — fa_decode_splitkv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with the partial states kept in a fixed array that the
+ * library holds on every GPU it runs on (FA_NOALLOC_SCRATCH_BYTES bytes per GPU, held until
+ * the process ends) instead of in a caller's workspace. The call allocates nothing; the
+ * caller still owns q, k, v, o and lse. Arguments, results and errors as in
+ * fa_decode_splitkv, plus:
+ *   - FA_ERR_WORKSPACE when fa_decode_workspace_bytes(B, H, d, num_splits) exceeds
+ *     FA_NOALLOC_SCRATCH_BYTES (at d = 128: when B*H*num_splits > 64,527);
+ *   - FA_ERR_HIP when the array's address cannot be obtained on the stream's device.
+ * The array is looked up on the stream's device (the current device for the null stream)
+ * at the first call there. All calls on one GPU share its array: calls that overlap in
+ * time on one GPU (on different streams, or from threads without ordering) race on it and
+ * must not be issued; calls ordered on one stream are safe. Nothing in the array needs to
+ * start at zero (every partial state a call reads, it wrote).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, float* o,
+                                    float* lse, int B, int H, int Nk, int d, float scale,
+                                    int num_splits, fa_dtype dtype, void* stream);
+
+/*
  * fa_decode_paged — fa_decode_splitkv over a paged key/value cache with per-sequence
  * lengths: the page indirection that serving engines pair with split-KV decoding
  * ("FlashAttention: Attention Is Limited by Memory, Not Math", section "Where it helps,

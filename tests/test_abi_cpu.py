@@ -284,3 +284,32 @@ def test_bias_python_layer_checks_without_gpu():
 ])
 def test_probe_mfma_rejects(args, status):
     assert fa.library().fa_probe_mfma(*args, None) == status
+
+
+def _noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, Nk=100, d=128, scale=0.1, S=8,
+             dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_decode_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                                                  a["B"], a["H"], a["Nk"], a["d"], a["scale"],
+                                                  a["S"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(Nk=0), fa.FA_ERR_SHAPE), (dict(S=0), fa.FA_ERR_SHAPE),
+    # partial states beyond the fixed scratch: (d + 2) * 4 bytes per (b, h, split)
+    (dict(B=64, H=64, S=16, d=128), fa.FA_ERR_WORKSPACE),
+    (dict(B=1, H=1, S=1, d=(32 << 20) // 4), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects_before_any_hip_call(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_decode_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+    assert fa.NOALLOC_SCRATCH_BYTES == 32 << 20
+    # the largest decode that fits at d = 128 (the header's example)
+    assert fa.decode_workspace_bytes(1, 1, 128, 64527) <= fa.NOALLOC_SCRATCH_BYTES
+    assert fa.decode_workspace_bytes(1, 1, 128, 64528) > fa.NOALLOC_SCRATCH_BYTES
