@@ -72,6 +72,25 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kNW = 8;  // waves per workgroup: two groups of four
 
+// Race check (a separate build, libfa_ldscheck.so, defines FA_LDS_POISON=1; the product
+// library does not): right before a direct load is issued into an LDS slot, the issuing
+// lane first overwrites that slot with NaN and waits for the write. The slot's previous
+// tile has then had its last reader (the barriers are meant to guarantee it), and the new
+// tile has not landed yet, so a wave that reads a slot too late (stale tile) or too early
+// (not yet landed) reads NaN, which turns into NaN or wrong values in O: with no race the
+// results are bitwise those of the product library.
+#ifndef FA_LDS_POISON
+#define FA_LDS_POISON 0
+#endif
+constexpr bool kPoison = FA_LDS_POISON != 0;
+
+// Fills one 16-byte LDS slot with NaN bit patterns (every bfloat16 half is 0xFFFF) and waits
+// until the write has completed, so that a direct load issued next lands on top of it.
+__device__ __forceinline__ void poison16(char* lds_slot) {
+  *(uint4*)lds_slot = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // dma16 with the non-temporal hint, for data read exactly once (the bias): it then does not
 // push out of L2 the K/V tiles that the other query tiles of a head read again (measured:
 // 5% faster biased prefill, no change in results).
@@ -247,6 +266,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   const int wg4 = w & 3;  // wave index within its group
   auto dma = [&](int t, char* dst, int n) {
     const int kv0 = t * BC;
+    if constexpr (kPoison) poison16(dst + (n * C::TL + 64 * wg4 + lane) * 16);
     const uint32_t lds = (uint32_t)(uintptr_t)((lds_char*)(dst + (n * C::TL + 64 * wg4) * 16));
     const int row = min(lrow + n * C::ROWSTEP, Nk - 1 - kv0);
     dma16((const char*)lbase + (size_t)kv0 * rs * 2, (uint32_t)(row * rs * 2) + lchunk, lds);
@@ -258,6 +278,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   auto issue = [&](int t, char* dst) {
     const int kv0 = t * BC;
     if (kv0 + BC <= Nk) {
+      if constexpr (kPoison)
+        for (int n = 0; n < C::LOADS; ++n) poison16(dst + (n * C::TL + 64 * wg4 + lane) * 16);
       const uint32_t lds0 = (uint32_t)(uintptr_t)((lds_char*)(dst + 64 * wg4 * 16));
       [&]<int... N>(std::integer_sequence<int, N...>) {
         (dma16_at<N * C::TL * 16>((const char*)lbase + (size_t)(kv0 + N * C::ROWSTEP) * rs * 2, loff, lds0), ...);
@@ -290,6 +312,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     const int cmax = (Nk - 1 - kv0) >> 3;
     const char* base = (const char*)(bw + kv0);
     char* dst = bias_buf(t);
+    if constexpr (kPoison)
+      for (int n = 0; n < BCfg::LOADS; ++n) poison16(dst + (n * 64 + lane) * 16);
     if (kv0 + BC <= Nk) {
 #pragma unroll
       for (int n = 0; n < BCfg::LOADS; ++n)
