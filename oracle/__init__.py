@@ -8,8 +8,8 @@ only the seeded input generators in ``workloads.py``.
 ``attention`` evaluates the plain definition O = softmax(Q K^T * scale + mask) V
 row by row in double precision (the C source states each passage it follows), with an
 optional additive bias on the scaled scores;
-``attention_bwd`` evaluates the gradients of sum(O * dO) with respect to Q, K, V
-from the same definition by the chain rule. ``paged_attention`` is the same definition
+``attention_bwd`` evaluates the gradients of sum(O * dO) with respect to Q, K, V (and,
+with a bias, with respect to a full bias) from the same definition by the chain rule. ``paged_attention`` is the same definition
 for one query per sequence whose keys and values live in a paged cache: it first
 gathers each sequence's logical key/value rows through its block table, then calls
 ``attention``. ``attention_varlen`` applies the definition to each sequence of a packed
@@ -70,6 +70,16 @@ def load_library(path: str):
                   ctypes.c_double, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    gb = lib.oracle_attention_bwd_bias
+    gb.restype = ctypes.c_int
+    gb.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong,
+                   ctypes.c_longlong,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_double, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
     return lib
 
 
@@ -199,13 +209,17 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
 
 
 def attention_bwd(q, k, v, do, scale: float, causal: bool = False, qrows=None, krows=None,
-                  threads: int | None = None):
-    """Float64 gradients of sum(O * dO) for O = attention(q, k, v).
+                  threads: int | None = None, bias=None, want_dbias: bool = False):
+    """Float64 gradients of sum(O * dO) for O = attention(q, k, v[, bias]).
 
-    q, do [B,H,Nq,d]; k, v [B,H,Nk,d]; all float32 or all bfloat16.
+    q, do [B,H,Nq,d]; k, v [B,H,Nk,d]; all float32, all bfloat16 or all float64.
     ``qrows``: flat query rows (b*H + h)*Nq + i whose dQ is returned (default all);
     ``krows``: flat key rows (b*H + h)*Nk + j whose dK and dV are returned (default all).
-    Returns (dq [nq, d], dk [nk, d], dv [nk, d]) float64.
+    ``bias``: optional CPU tensor broadcastable to [B, H, Nq, Nk], added to the scaled
+    scores as in ``attention``; with ``want_dbias`` the gradient with respect to a full
+    [B, H, Nq, Nk] bias is returned too (dL/dbias = dS; every query row, qrows None).
+    Returns (dq [nq, d], dk [nk, d], dv [nk, d]) float64, and dbias [B*H*Nq, Nk] float64
+    when want_dbias.
     """
     qa, dt = _as_input(q)
     ka, dtk = _as_input(k)
@@ -232,15 +246,27 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, qrows=None, k
     dq = np.empty((nq, d), np.float64)
     dk = np.empty((nk, d), np.float64)
     dv = np.empty((nk, d), np.float64)
-    rc = _load().oracle_attention_bwd(
-        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, dt, B, H, Nq, Nk, d,
-        float(scale), _causal_code(causal),
-        qr.ctypes.data if qr is not None else None, nq,
-        kr.ctypes.data if kr is not None else None, nk, threads,
-        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    rows_args = (qr.ctypes.data if qr is not None else None, nq,
+                 kr.ctypes.data if kr is not None else None, nk, threads,
+                 dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if bias is None:
+        if want_dbias:
+            raise ValueError("want_dbias needs a bias")
+        rc = _load().oracle_attention_bwd(
+            qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, dt, B, H, Nq, Nk, d,
+            float(scale), _causal_code(causal), *rows_args)
+        if rc != 0:
+            raise ValueError("oracle_attention_bwd rejected its arguments")
+        return dq, dk, dv
+    bt, bcode, (sb, sh, sq) = _bias_view(bias, B, H, Nq, Nk)
+    db = np.empty((B * H * Nq, Nk), np.float64) if want_dbias else None
+    rc = _load().oracle_attention_bwd_bias(
+        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, dt, bt.data_ptr(), bcode,
+        sb, sh, sq, B, H, Nq, Nk, d, float(scale), _causal_code(causal), *rows_args,
+        db.ctypes.data if db is not None else None)
     if rc != 0:
-        raise ValueError("oracle_attention_bwd rejected its arguments")
-    return dq, dk, dv
+        raise ValueError("oracle_attention_bwd_bias rejected its arguments")
+    return (dq, dk, dv, db) if want_dbias else (dq, dk, dv)
 
 
 def paged_gather(cache, block_table, seq_len: int, b: int, page_size: int):

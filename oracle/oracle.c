@@ -235,23 +235,29 @@ int oracle_attention_bias(const void* q, const void* k, const void* v, int dtype
  */
 static void row_stats(const void* q, const void* k, const void* v, const void* dout,
                       int dtype, int H, int Nq, int Nk, int d, double scale, int causal,
+                      const bias_view* bias,
                       long long r, double* s, double* o, double* lse, double* dsum) {
-  one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, NULL, r, s, o, lse, NULL);
+  one_row(q, k, v, dtype, H, Nq, Nk, d, scale, causal, bias, r, s, o, lse, NULL);
   double acc = 0.0;
   for (int t = 0; t < d; ++t) acc += widen(dout, dtype, (size_t)r * d + t) * o[t];
   *dsum = acc;
 }
 
-/* score of (query row r, key j of the same head) or -inf when masked */
-static double score(const void* q, const void* k, int dtype, int Nq, int Nk, int d,
-                    double scale, int causal, long long r, int j) {
+/* score of (query row r, key j of the same head), plus the bias element of the pair if
+ * there is a bias, or -inf when masked */
+static double score(const void* q, const void* k, int dtype, int H, int Nq, int Nk, int d,
+                    double scale, int causal, const bias_view* bias, long long r, int j) {
   long long bh = r / Nq;
   int i = (int)(r % Nq);
   if (causal && (long long)j - query_offset(causal, Nq, Nk) > (long long)i) return -INFINITY;
   size_t qoff = (size_t)r * d, koff = ((size_t)bh * Nk + j) * d;
   double dot = 0.0;
   for (int t = 0; t < d; ++t) dot += widen(q, dtype, qoff + t) * widen(k, dtype, koff + t);
-  return scale * dot;
+  double sc = scale * dot;
+  if (bias && bias->p)
+    sc += widen(bias->p, bias->dtype,
+                (size_t)((bh / H) * bias->sb + (bh % H) * bias->sh + (long long)i * bias->sq + j));
+  return sc;
 }
 
 /* dP_ij = dO_i . v_j */
@@ -265,7 +271,8 @@ static double dprob(const void* dout, const void* v, int dtype, int Nq, int Nk, 
 }
 
 /*
- * oracle_attention_bwd
+ * oracle_attention_bwd (bwd_rows below, with no bias; oracle_attention_bwd_bias at the end
+ * of the file adds one)
  *   q [B][H][Nq][d], k, v [B][H][Nk][d], dout [B][H][Nq][d], one dtype.
  *   qrows : flat query rows (b*H + h)*Nq + i whose dQ is wanted (nq of them),
  *           or NULL for all;  dq : [nq][d] doubles (may be NULL if nq == 0).
@@ -274,15 +281,21 @@ static double dprob(const void* dout, const void* v, int dtype, int Nq, int Nk, 
  *   nthreads : OpenMP threads. Returns 0, or -1 for an invalid argument or a
  *   failed allocation.
  */
-int oracle_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
-                         int dtype, int B, int H, int Nq, int Nk, int d, double scale,
-                         int causal, const long long* qrows, long long nq,
-                         const long long* krows, long long nk, int nthreads,
-                         double* dq, double* dk, double* dv) {
+static int bwd_rows(const void* q, const void* k, const void* v, const void* dout,
+                    int dtype, int B, int H, int Nq, int Nk, int d, double scale,
+                    int causal, const bias_view* bias, const long long* qrows, long long nq,
+                    const long long* krows, long long nk, int nthreads,
+                    double* dq, double* dk, double* dv, double* dbias) {
   if (!q || !k || !v || !dout) return -1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nthreads < 1) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
   if (causal < 0 || causal > 2) return -1;
+  if (bias && bias->p) {
+    if (bias->dtype != ORACLE_F32 && bias->dtype != ORACLE_BF16 && bias->dtype != ORACLE_F64) return -1;
+    if (bias->sb < 0 || bias->sh < 0 || bias->sq < 0) return -1;
+  }
+  /* the bias gradient is the full dS of every query row */
+  if (dbias && qrows) return -1;
   const long long BH = (long long)B * H;
   if (!qrows) nq = BH * Nq;
   if (!krows) nk = BH * Nk;
@@ -310,13 +323,17 @@ int oracle_attention_bwd(const void* q, const void* k, const void* v, const void
       double* out = dq + (size_t)n * d;
       for (int t = 0; t < d; ++t) out[t] = 0.0;
       if (!s || !o) continue;
-      row_stats(q, k, v, dout, dtype, H, Nq, Nk, d, scale, causal, r, s, o, &lse, &dsum);
+      double* grow = dbias ? dbias + (size_t)n * Nk : NULL;
+      if (grow) for (int j = 0; j < Nk; ++j) grow[j] = 0.0;
+      row_stats(q, k, v, dout, dtype, H, Nq, Nk, d, scale, causal, bias, r, s, o, &lse, &dsum);
       if (lse == -INFINITY) continue; /* empty row: P = 0 */
       for (int j = 0; j < Nk; ++j) {
-        double sc = score(q, k, dtype, Nq, Nk, d, scale, causal, r, j);
+        double sc = score(q, k, dtype, H, Nq, Nk, d, scale, causal, bias, r, j);
         if (sc == -INFINITY) continue;
         double p = exp(sc - lse);
         double ds = p * (dprob(dout, v, dtype, Nq, Nk, d, r, j) - dsum);
+        /* the bias enters S with weight 1, so dL/dbias_ij = dS_ij */
+        if (grow) grow[j] = ds;
         size_t koff = ((size_t)bh * Nk + j) * d;
         for (int t = 0; t < d; ++t) out[t] += scale * ds * widen(k, dtype, koff + t);
       }
@@ -347,7 +364,7 @@ int oracle_attention_bwd(const void* q, const void* k, const void* v, const void
 #pragma omp for schedule(dynamic, 16)
     for (long long r = 0; r < BH * Nq; ++r) {
       if (!need[r / Nq] || !s || !o) continue;
-      row_stats(q, k, v, dout, dtype, H, Nq, Nk, d, scale, causal, r, s, o,
+      row_stats(q, k, v, dout, dtype, H, Nq, Nk, d, scale, causal, bias, r, s, o,
                 lse_all + r, dsum_all + r);
     }
     free(s);
@@ -370,7 +387,7 @@ int oracle_attention_bwd(const void* q, const void* k, const void* v, const void
     for (int i = 0; i < Nq; ++i) {
       long long r = bh * Nq + i;
       if (lse_all[r] == -INFINITY) continue;
-      double sc = score(q, k, dtype, Nq, Nk, d, scale, causal, r, j);
+      double sc = score(q, k, dtype, H, Nq, Nk, d, scale, causal, bias, r, j);
       if (sc == -INFINITY) continue;
       double p = exp(sc - lse_all[r]);
       double ds = p * (dprob(dout, v, dtype, Nq, Nk, d, r, j) - dsum_all[r]);
@@ -383,4 +400,34 @@ int oracle_attention_bwd(const void* q, const void* k, const void* v, const void
   }
   free(need); free(lse_all); free(dsum_all);
   return 0;
+}
+
+int oracle_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
+                         int dtype, int B, int H, int Nq, int Nk, int d, double scale,
+                         int causal, const long long* qrows, long long nq,
+                         const long long* krows, long long nk, int nthreads,
+                         double* dq, double* dk, double* dv) {
+  return bwd_rows(q, k, v, dout, dtype, B, H, Nq, Nk, d, scale, causal, NULL, qrows, nq,
+                  krows, nk, nthreads, dq, dk, dv, NULL);
+}
+
+/*
+ * oracle_attention_bwd_bias: oracle_attention_bwd for the attention with the additive
+ * bias of oracle_attention_bias (S = scale * Q K^T + bias, the same strides and dtypes),
+ * and optionally the gradient with respect to a full bias:
+ *   dbias : [B*H*Nq][Nk] doubles or NULL. The bias enters each score with weight 1, so
+ *           dL/dbias_ij = dS_ij (0 for pairs the mask hides and rows that see no key).
+ *           A broadcast bias's gradient is this summed over its broadcast dimensions.
+ *           Requires qrows == NULL (every query row).
+ */
+int oracle_attention_bwd_bias(const void* q, const void* k, const void* v, const void* dout,
+                              int dtype, const void* bias, int bdtype, long long sb,
+                              long long sh, long long sq, int B, int H, int Nq, int Nk, int d,
+                              double scale, int causal, const long long* qrows, long long nq,
+                              const long long* krows, long long nk, int nthreads,
+                              double* dq, double* dk, double* dv, double* dbias) {
+  if (!bias) return -1;
+  bias_view bv = {bias, bdtype, sb, sh, sq};
+  return bwd_rows(q, k, v, dout, dtype, B, H, Nq, Nk, d, scale, causal, &bv, qrows, nq,
+                  krows, nk, nthreads, dq, dk, dv, dbias);
 }
