@@ -19,9 +19,10 @@ MUTANTS = {
     "bias subtracted": (ADD, ADD.replace("s[j] +=", "s[j] -=")),
     "bias multiplied by the scale": (ADD, ADD.replace("s[j] += widen", "s[j] += scale * widen")),
     "bias dropped": (ADD, ADD.replace("if (bias && bias->p)", "if (0)")),
-    "bias row of query 0 for every query": ("(long long)i * bias->sq", "0LL * bias->sq"),
-    "bias ignores the batch index": ("(bh / H) * bias->sb", "0 * bias->sb"),
-    "bias ignores the head index": ("(bh % H) * bias->sh", "0 * bias->sh"),
+    "bias row of query 0 for every query": ("(long long)i * bias->sq);", "0LL * bias->sq);"),
+    "bias ignores the batch index": ("brow = (size_t)((bh / H) * bias->sb", "brow = (size_t)(0 * bias->sb"),
+    "bias ignores the head index": ("(bh / H) * bias->sb + (bh % H) * bias->sh + (long long)i * bias->sq);",
+                                    "(bh / H) * bias->sb + 0 * bias->sh + (long long)i * bias->sq);"),
     "bias also un-hides masked keys": (
         "if ((long long)j > last_visible) { s[j] = -INFINITY; continue; }",
         "if ((long long)j > last_visible && !(bias && bias->p)) { s[j] = -INFINITY; continue; }"),
