@@ -13,6 +13,7 @@ not on the GPU, the call raises.
     o, lse = decode_noalloc(q, k, v, num_splits=64)         # the same, no device allocation
     o, lse = decode_paged(q, k_cache, v_cache, block_table, seq_lens)  # paged cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, scale=None, causal=False)   # gradients
+    dq, dk, dv[, dbias] = bwd_bias(q, k, v, bias, o, lse, do)         # ... of fwd_bias
 
 Shapes are [B, H, N, d] (d innermost, contiguous); o is float32 [B, H, Nq, d],
 lse float32 [B, H, Nq]. The C header include/fa.h states the full contract.
@@ -23,7 +24,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_bias", "pad_bias", "fwd_fp8", "fwd_varlen", "decode", "decode_noalloc", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_workspace_bytes", "status_str", "NOALLOC_SCRATCH_BYTES",
+__all__ = ["fwd", "fwd_bias", "pad_bias", "fwd_fp8", "fwd_varlen", "decode", "decode_noalloc", "decode_paged", "decode_workspace_bytes", "bwd", "bwd_bias", "bwd_workspace_bytes", "status_str", "NOALLOC_SCRATCH_BYTES",
            "library", "FaError", "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
            "FA_ERR_HIP", "FA_ERR_VALUE", "FA_ERR_ALIGN", "FA_BF16", "FA_F32", "EXPORTS"]
 
@@ -39,7 +40,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_bias", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv",
            "fa_decode_splitkv_noalloc", "fa_decode_paged",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_probe_mfma", "fa_status_str", "fa_last_hip_error",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_bias", "fa_probe_mfma", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -58,6 +59,9 @@ _SIGS = {
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _sz, _i, _vp]),
+    "fa_bwd_bias": (_i, [_vp, _vp, _vp, _vp, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                         _i, _vp]),
     "fa_probe_mfma": (_i, [_vp, _sz, _i, _i, _vp]),
     "fa_status_str": (ctypes.c_char_p, [_i]),
     "fa_last_hip_error": (_i, []),
@@ -480,3 +484,43 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, d
         _dtype_code(q), _stream_ptr(q.device))
     _raise(st, "fa_bwd")
     return dq, dk, dv
+
+
+def bwd_bias(q, k, v, bias, o, lse, do, scale: float | None = None, causal=False, dq=None,
+             dk=None, dv=None, want_dbias: bool = False, dbias=None, workspace=None):
+    """Backward of fwd_bias: (dq, dk, dv) float32, plus dbias (float32 [B, H, Nq, Nk], the
+    gradient of a full bias: dS) when want_dbias or a dbias tensor is given. bias as for
+    fwd_bias (bfloat16, rows padded with pad_bias); o and lse are fwd_bias's outputs. For a
+    bias shared along some dimensions, its gradient is dbias summed over them."""
+    import torch
+    _check_inputs(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise NotImplementedError("bwd_bias takes bfloat16 q, k, v")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    be, sb, sh, sq = _bias_strides(bias, q, B, H, Nq, Nk)
+    if not isinstance(do, torch.Tensor) or do.shape != q.shape or do.dtype != q.dtype \
+            or not do.is_contiguous() or do.device != q.device:
+        raise ValueError("do must be a contiguous tensor of q's shape, dtype and device")
+    if not isinstance(o, torch.Tensor) or o.shape != (B, H, Nq, d) or o.dtype != torch.float32 \
+            or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be the contiguous float32 [B, H, Nq, d] output of fwd_bias")
+    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, Nq) or lse.dtype != torch.float32 \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be the contiguous float32 [B, H, Nq] output of fwd_bias")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = _out_arg(dq, (B, H, Nq, d), q.device, "dq")
+    dk = _out_arg(dk, (B, H, Nk, d), q.device, "dk")
+    dv = _out_arg(dv, (B, H, Nk, d), q.device, "dv")
+    if want_dbias or dbias is not None:
+        dbias = _out_arg(dbias, (B, H, Nq, Nk), q.device, "dbias")
+    workspace = _workspace_arg(workspace, bwd_workspace_bytes(B, H, Nq), q.device)
+    st = library().fa_bwd_bias(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), be.data_ptr(), sb, sh, sq, o.data_ptr(),
+        lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        dbias.data_ptr() if dbias is not None else None, B, H, Nq, Nk, d, float(scale),
+        _causal_arg(causal), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _dtype_code(q), _stream_ptr(q.device))
+    _raise(st, "fa_bwd_bias")
+    return (dq, dk, dv, dbias) if dbias is not None else (dq, dk, dv)

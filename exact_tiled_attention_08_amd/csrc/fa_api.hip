@@ -373,7 +373,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   const long long nqt = (Nq + fa::kBwdQueryRows - 1) / fa::kBwdQueryRows;
   if (BH * nkt > INT32_MAX || BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
 
-  fa::BwdParams p;
+  fa::BwdParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -398,6 +398,70 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   if (dtype == FA_F32) return finish_launch(fa::launch_bwd_f32(p, d, causal != 0, (hipStream_t)stream));
   return finish_launch(fa::launch_bwd(p, d, causal != 0, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      const float* o, const float* lse, const void* dout, float* dq, float* dk,
+                      float* dv, float* dbias, int B, int H, int Nq, int Nk, int d, float scale,
+                      int causal, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                      void* stream) {
+  if (!q || !k || !v || !bias || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX) return FA_ERR_SHAPE;
+  if (bias_stride_b < 0 || bias_stride_h < 0 || bias_stride_q < 0) return FA_ERR_SHAPE;
+  const long long lim = (1LL << 62) / 4;
+  if (bias_stride_b > lim / B || bias_stride_h > lim / H || bias_stride_q > lim / Nq)
+    return FA_ERR_SHAPE;
+  if (dbias && BH * (long long)Nq > lim / Nk) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > kMaxHeadElems || (long long)Nq * d > kMaxHeadElems) return FA_ERR_UNSUPPORTED;
+  // the bias rows of one 64-query tile are addressed with 32-bit byte offsets
+  if (bias_stride_q * 128 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, Nq);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      !aligned16(bias) || (dbias && !aligned16(dbias)) || ((uintptr_t)lse & 3u) != 0 ||
+      (bias_stride_b | bias_stride_h | bias_stride_q) % 8 != 0)
+    return FA_ERR_ALIGN;
+  const long long nkt = (Nk + fa::kBwdKeyRows - 1) / fa::kBwdKeyRows;
+  const long long nqt = (Nq + fa::kBwdQueryRows - 1) / fa::kBwdQueryRows;
+  if (BH * nkt > INT32_MAX || BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws = (float*)workspace;
+  p.BH = (int)BH;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.Nq_pad = (int)(nqt * fa::kBwdQueryRows);
+  p.off = query_offset(causal, Nq, Nk);
+  p.nkt = (int)nkt;
+  p.nqt = (int)nqt;
+  p.hpg_kv = heads_per_group((int)BH, nkt);
+  p.hpg_q = heads_per_group((int)BH, nqt);
+  p.scale = scale;
+  p.c = scale * fa::kLog2e;
+  p.bias = bias;
+  p.bsb = bias_stride_b;
+  p.bsh = bias_stride_h;
+  p.bsq = bias_stride_q;
+  p.H = H;
+  p.dbias = dbias;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  return finish_launch(fa::launch_bwd_bias(p, d, causal != 0, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -152,10 +152,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, bool CAUSAL>
+// BIAS: the scores carry the additive bias of fa_fwd_bias (S = scale QK^T + bias), staged
+// per query tile as a [64 query][128 key] bfloat16 tile next to Q and dO, with the same
+// 256-byte-row swizzle, and read per lane (one key, 16 queries per step) with the same
+// transpose reads as Q^T. DBIAS: dS, the gradient of a full bias, is also written out.
+template <int D, bool CAUSAL, bool BIAS = false, bool DBIAS = false>
 __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   using C = BCfg<D>;
-  constexpr int STAGE = 2 * C::TILEB + 512;  // Q tile, dO tile, 64 LSE2 + 64 D values
+  constexpr int BTILE = kRows * 2 * kBwdKeyRows;             // bias tile, 256-byte rows
+  constexpr int BOFF = 2 * C::TILEB + 512;                    // its offset inside a stage
+  constexpr int STAGE = BOFF + (BIAS ? BTILE : 0);  // Q tile, dO tile, 64 LSE2 + 64 D, bias
+  static_assert(!DBIAS || BIAS, "the bias gradient needs the biased scores");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -176,6 +183,12 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   const __bf16* __restrict__ kh = (const __bf16*)p.k + (size_t)bh * p.Nk * D;
   const __bf16* __restrict__ vh = (const __bf16*)p.v + (size_t)bh * p.Nk * D;
   const float* __restrict__ wsh = p.ws + (size_t)bh * p.Nq_pad * 2;
+  // bias of (b, h), query 0, key k0 (BIAS only)
+  const uint16_t* biasw = nullptr;
+  if constexpr (BIAS) {
+    const int b = bh / p.H;
+    biasw = (const uint16_t*)p.bias + (size_t)b * p.bsb + (size_t)(bh - b * p.H) * p.bsh + k0;
+  }
 
   // K and V rows of this lane's key: the B operands of S = Q K^T and dP = dO V^T. Keys past
   // Nk are zero; their columns are independent of every other column and are not stored.
@@ -212,6 +225,19 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
       dma16(qh + (size_t)r0 * D, off, lds_addr(st + dst));
       dma16(doh + (size_t)r0 * D, off, lds_addr(st + C::TILEB + dst));
     }
+    if constexpr (BIAS) {
+      // 64 rows x 16 chunks: slot n*kT + tid is row tid/16 + 16n at chunk position tid%16,
+      // holding chunk (position ^ swizzle); rows past Nq repeat row Nq-1 and chunks at or
+      // past Nk the chunk of key Nk-1 (their pairs are masked or not stored)
+      const int brow = tid >> 4;
+      const int bch = min((tid & 15) ^ bswz<16>(brow), (p.Nk - 1 - k0) >> 3);
+      const char* base = (const char*)(biasw + (size_t)r0 * p.bsq);
+      const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(st + BOFF + 64 * w * 16));
+      [&]<int... N>(std::integer_sequence<int, N...>) {
+        ((dma16(base, (uint32_t)(((long long)min(brow + 16 * N, p.Nq - 1 - r0) * p.bsq + 8 * bch) * 2),
+                lbase + N * kT * 16)), ...);
+      }(std::make_integer_sequence<int, BTILE / (16 * kT)>{});
+    }
     // 512 bytes of statistics: lanes 0..15 the LSE2 values, 16..31 the D values
     if (w == 0 && lane < 32) dma16(wsh + (size_t)t * 128, 16u * lane, lds_addr(st + 2 * C::TILEB));
   };
@@ -237,11 +263,20 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   // MFMAs and that of step 1 over group 2's, so the matrix core and the vector ALU of the
   // SIMD work at the same time.
   auto tile_stream = [&](auto maskedc, const char* Qs, const char* dOs, const float* sts,
-                         const f32x16 (&sinit)[2]) {
+                         const f32x16 (&sinit)[2], const char* Bs, int qa0) {
     constexpr bool MASKED = decltype(maskedc)::value;
     constexpr int NG = D / 8, NF = 4 * NG, RING = 6, EPM = 16 / NG;  // elements per MFMA
     f32x16 s[2], dp[2];
     bf16x8 pb[2][2], dsb[2][2];
+    // bias of element e of step x (query 32x + 8(e/4) + 4g + e%4, this lane's key): two
+    // transpose reads per step from the [query][key] tile
+    bf16x8 bb[2][2];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bb[x][h] = tfrag<kBwdKeyRows>(Bs, 32 * x + 16 * h, w, lane);
+    }
     f32x4 L[2], Dv[2];  // LSE2 and D of one group of 4 elements, double-buffered
     bf16x8 fr[RING];
     auto frag = [&](auto fc) -> bf16x8 {
@@ -264,14 +299,26 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     float pe_t[2][EPM], sd_t[2][EPM];
     auto front = [&](auto xc, auto ec, auto bc) {
       constexpr int x = decltype(xc)::value, e = decltype(ec)::value, b = decltype(bc)::value;
-      pe_t[b][e % EPM] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x][e], p.c, -L[(e >> 2) & 1][e & 3]));
+      if constexpr (BIAS) {  // (s * scale + bias) in log2 units
+        const float sb = __builtin_fmaf(s[x][e], p.scale, (float)bb[x][e >> 3][e & 7]);
+        pe_t[b][e % EPM] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb, kLog2e, -L[(e >> 2) & 1][e & 3]));
+      } else {
+        pe_t[b][e % EPM] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x][e], p.c, -L[(e >> 2) & 1][e & 3]));
+      }
       sd_t[b][e % EPM] = dp[x][e] - Dv[(e >> 2) & 1][e & 3];
     };
     auto back = [&](auto xc, auto ec, auto bc) {
       constexpr int x = decltype(xc)::value, e = decltype(ec)::value, b = decltype(bc)::value;
       const float pe = pe_t[b][e % EPM];
       pb[x][e >> 3][e & 7] = (__bf16)pe;
-      dsb[x][e >> 3][e & 7] = (__bf16)(pe * sd_t[b][e % EPM]);
+      if constexpr (DBIAS) {
+        const float ds = pe * sd_t[b][e % EPM];
+        dsb[x][e >> 3][e & 7] = (__bf16)ds;
+        const int qi = qa0 + 32 * x + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (qi < p.Nq && key < p.Nk) p.dbias[((size_t)bh * p.Nq + qi) * p.Nk + key] = ds;
+      } else {
+        dsb[x][e >> 3][e & 7] = (__bf16)(pe * sd_t[b][e % EPM]);
+      }
     };
     auto step = [&](auto fc) {
       constexpr int f = decltype(fc)::value, grp = f / NG, i = f % NG;
@@ -319,6 +366,23 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     }(std::make_integer_sequence<int, NF>{});
   };
 
+  // dS = 0 for query rows [r_begin, r_end) and this wave's 32 keys (pairs the causal mask
+  // hides in tiles that are not visited): 8 rows of 32 keys per store of the wave, 4 keys
+  // per lane.
+  auto zero_dbias = [&](int r_begin, int r_end) {
+    const int kq = kw0 + 4 * (lane & 7);
+    for (int r = r_begin + (lane >> 3); r < r_end; r += 8) {
+      float* row = p.dbias + ((size_t)bh * p.Nq + r) * p.Nk;
+      if (kq + 3 < p.Nk && ((p.Nk & 3) == 0)) {
+        *(f32x4*)(row + kq) = f32x4{};
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (kq + u < p.Nk) row[kq + u] = 0.f;
+      }
+    }
+  };
+
   // Tiles before tm hold a query that misses a key of this workgroup (causal): they take
   // the masked stream; from tm on every pair is visible and the stream has no mask.
   const int tm = CAUSAL ? min(t1, max(t0, (k0 + kBwdKeyRows - 1 - p.off + kRows - 1) / kRows)) : t0;
@@ -334,8 +398,11 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int qa0 = t * kRows;
     f32x16 sinit[2] = {f32x16{}, f32x16{}};
     if constexpr (MASKED) {
-      // no query of this tile sees a key of this wave: nothing to add
-      if (qa0 + kRows - 1 + p.off < kw0) return;
+      // no query of this tile sees a key of this wave: nothing to add (dS = 0 there)
+      if (qa0 + kRows - 1 + p.off < kw0) {
+        if constexpr (DBIAS) zero_dbias(qa0, min(qa0 + kRows, p.Nq));
+        return;
+      }
       // Masked pairs enter as S = -inf through the initial accumulator of the S product, so
       // that P = exp2(-inf) = 0 and dS = 0 with no extra work in the stream; element e of
       // step x is query qa0 + 32x + 8(e/4) + 4g + e%4 and is masked iff key > query + off.
@@ -347,7 +414,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) sinit[x][e] = (8 * (e >> 2) + (e & 3) < lim) ? -INFINITY : 0.f;
       }
     }
-    tile_stream(maskedc, Qs, dOs, sts, sinit);
+    tile_stream(maskedc, Qs, dOs, sts, sinit, Qs + BOFF, qa0);
   };
   auto pin = [](f32x16 (&a)[D / 32], f32x16 (&b)[D / 32]) {
 #pragma unroll
@@ -361,6 +428,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   wait_loads();
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
+  if constexpr (DBIAS && CAUSAL) zero_dbias(0, min(t0 * kRows, p.Nq));  // tiles not visited
   int t = t0;
   for (; t < tm; ++t) {
     body(t, std::true_type{});
@@ -393,11 +461,18 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, bool CAUSAL>
+// BIAS: the scores carry the additive bias of fa_fwd_bias. Each wave stages the bias of its
+// own 32 query rows for the current 64-key tile (4 KB, one buffer per wave) with direct
+// loads issued right after the tile's barrier, and reads 4 keys per 8-byte read in the
+// S^T layout (one query per lane column); 16-byte chunks are XOR-swizzled by (row / 2) % 8
+// against bank conflicts (as in the biased prefill).
+template <int D, bool CAUSAL, bool BIAS = false>
 __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   using C = BCfg<D>;
   constexpr int STAGE = 2 * C::TILEB;  // K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int WBIAS = 32 * kRows * 2;                   // one wave's bias rows of a tile
+  constexpr int BOFF = 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + (BIAS ? 4 * WBIAS : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -464,6 +539,43 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // Bias rows of this wave (BIAS only): row r of the wave (query wq0 + r, clamped to Nq-1)
+  // starts at bwv + r*bsq; direct load n of lane L fills row 8n + L/8, chunk position L%8,
+  // which holds chunk position ^ ((row / 2) % 8) of the row's 64 keys.
+  const uint16_t* bwv = nullptr;
+  char* const bwl = smem + BOFF + w * WBIAS;
+  uint32_t boff[4];
+  if constexpr (BIAS) {
+    const int b = bh / p.H;
+    const int r0 = min(wq0, p.Nq - 1);
+    bwv = (const uint16_t*)p.bias + (size_t)b * p.bsb + (size_t)(bh - b * p.H) * p.bsh + (size_t)r0 * p.bsq;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int r = 8 * n + (lane >> 3);
+      const int dr = min(wq0 + r, p.Nq - 1) - r0;
+      boff[n] = (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    }
+  }
+  auto bias_issue = [&](int t) {
+    const int ka = t * kRows;
+    const char* base = (const char*)(bwv + ka);
+    if (ka + kRows <= p.Nk) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) dma16(base, boff[n], lds_addr(bwl + n * 64 * 16));
+      return;
+    }
+    // the key tail: chunks at or past Nk take the chunk of key Nk-1 (masked anyway)
+    const int cmax = (p.Nk - 1 - ka) >> 3;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int r = 8 * n + (lane >> 3);
+      const int dr = min(wq0 + r, p.Nq - 1) - min(wq0, p.Nq - 1);
+      const int ch = min((lane & 7) ^ ((r >> 1) & 7), cmax);
+      const uint32_t off = (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)ch;
+      dma16(base, off, lds_addr(bwl + n * 64 * 16));
+    }
+  };
+
   f32x16 dq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
@@ -473,6 +585,8 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
     const int cur = t & 1;
     wait_loads();
     wg_barrier();
+    // this wave's bias rows of tile t, before the next tile's loads (loads complete in order)
+    if constexpr (BIAS) bias_issue(t);
     if (t + 1 < ntiles) issue(t + 1, stage(cur ^ 1));
     const char* Ks = stage(cur);
     const char* Vs = Ks + C::TILEB;
@@ -489,10 +603,29 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
       // element i: key ka + 8(i/4) + 4g + i%4, query qrow
       const bool need_mask = (ka + 32 > p.Nk) || (CAUSAL && ka + 31 > wq0 + p.off);
       const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - ka - 4 * g;
+      if constexpr (BIAS) {
+        // s <- s * scale + bias, in natural-log units; keys ka + 8q + 4g + 0..3 sit at byte
+        // 8g of chunk position (4kb + q) ^ ((col / 2) % 8) of this lane's row
+        if (kb == 0) {
+          if (t + 1 < ntiles)
+            wait_loads_but<2 * C::LOADS>();  // the bias, not the next tile's K and V
+          else
+            wait_loads();
+        }
+        const char* brow = bwl + col * (kRows * 2);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const v4i16 raw = *(const v4i16*)(brow + (((4 * kb + qd) ^ ((col >> 1) & 7)) << 4) + 8 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[4 * qd + e] = __builtin_fmaf(s[4 * qd + e], p.scale,
+                                           __uint_as_float((uint32_t)(uint16_t)raw[e] << 16));
+        }
+      }
       bf16x8 dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], BIAS ? kLog2e : p.c, -lse2));
         if (need_mask && 8 * (i >> 2) + (i & 3) > lim) pe = 0.f;
         dsb[i >> 3][i & 7] = (__bf16)(pe * (dp[i] - dsum));
       }
@@ -519,7 +652,7 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool BIAS = false>
 hipError_t launch(const BwdParams& prm, bool causal, hipStream_t s) {
   BwdParams p = prm;
   constexpr int RPB = 256 / (D / 8);
@@ -528,7 +661,21 @@ hipError_t launch(const BwdParams& prm, bool causal, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned nkv = (unsigned)(p.BH * p.nkt), nq = (unsigned)(p.BH * p.nqt);
-  if (causal) {
+  if constexpr (BIAS) {
+    if (causal) {
+      if (p.dbias)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, true>), dim3(nkv), dim3(kT), 0, s, p);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, false>), dim3(nkv), dim3(kT), 0, s, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3(nq), dim3(kT), 0, s, p);
+    } else {
+      if (p.dbias)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, true>), dim3(nkv), dim3(kT), 0, s, p);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, false>), dim3(nkv), dim3(kT), 0, s, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), dim3(nq), dim3(kT), 0, s, p);
+    }
+  } else if (causal) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(nkv), dim3(kT), 0, s, p);
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(nq), dim3(kT), 0, s, p);
   } else {
@@ -543,6 +690,11 @@ hipError_t launch(const BwdParams& prm, bool causal, hipStream_t s) {
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
   if (d == 128) return launch<128>(p, causal, s);
   return launch<64>(p, causal, s);
+}
+
+hipError_t launch_bwd_bias(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return launch<128, true>(p, causal, s);
+  return launch<64, true>(p, causal, s);
 }
 
 }  // namespace fa

@@ -98,6 +98,15 @@ struct BwdParams {
   int hpg_q;          // (b, h) pairs per XCD group, dQ kernel
   float scale;
   float c;            // scale * log2(e)
+  // Additive bias only (the backward of fa_fwd_bias): element (b, h, i, j) at
+  // bias[b*bsb + h*bsh + i*bsq + j] (bfloat16), H gives b and h of a pair; dbias, if not
+  // null, receives dL/dbias = dS as a full float32 [B][H][Nq][Nk] tensor.
+  const void* bias;
+  long long bsb;
+  long long bsh;
+  long long bsq;
+  int H;
+  float* dbias;
 };
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence would also wait
@@ -165,6 +174,7 @@ hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStrea
 // with hipGetSymbolAddress, then cached); FA_NOALLOC_SCRATCH_BYTES long.
 hipError_t decode_scratch(int device, void** ptr);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_bias(const BwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 // Query rows per workgroup of each prefill kernel (host needs it for the grid).

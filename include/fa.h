@@ -252,6 +252,31 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
                  fa_dtype dtype, void* stream);
 
 /*
+ * fa_bwd_bias — fa_bwd for the attention of fa_fwd_bias (S = scale * Q K^T + bias): the
+ * gradients with respect to q, k and v of a loss L, given do = dL/dO and the o and lse
+ * that fa_fwd_bias returned for the same q, k, v, bias, scale and causal; optionally also
+ * the gradient with respect to a full bias. The bias enters each score with weight 1, so
+ * dL/dbias_ij = dS_ij = P_ij (dP_ij - rowsum(dO * O)_i) ("Explain FlashAttention ...",
+ * section "Exact attention, finite precision and backward": the backward covers the masks
+ * and biases the forward supports).
+ *   bias, bias_stride_b/h/q: as in fa_fwd_bias (FA_BF16 rules: 16-byte aligned, strides
+ *   multiples of 8, each row readable to its first Nk elements rounded up to 8);
+ *   bias_stride_q * 128 < 2^31.
+ *   dbias: NULL, or float32 [B][H][Nq][Nk] (16-byte aligned), written in full: dS for every
+ *   (query, key) pair, 0 where the mask or a -inf bias hides the pair. It is the gradient of
+ *   a full bias; the gradient of a bias that is shared along some dimensions (a stride of 0)
+ *   is its sum over those dimensions, which the caller forms.
+ *   Other arguments, layouts, workspace and errors as in fa_bwd; dtype FA_BF16 only
+ *   (FA_F32 returns FA_ERR_UNSUPPORTED).
+ */
+fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                      const float* o, const float* lse, const void* dout, float* dq, float* dk,
+                      float* dv, float* dbias, int B, int H, int Nq, int Nk, int d, float scale,
+                      int causal, void* workspace, size_t workspace_bytes, fa_dtype dtype,
+                      void* stream);
+
+/*
  * fa_probe_mfma — measurement aid, not part of the attention method: launches `blocks`
  * workgroups of 256 threads in which every wave issues 4 * iters back-to-back
  * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on register operands, with no memory traffic,
