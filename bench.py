@@ -63,6 +63,22 @@ LAST_WARMUP = {}  # untimed warm-up of the latest time_launches call (launches, 
 
 
 WARMUP_SECONDS = 2.0  # untimed warm-up of each leg after its `warmup` steps (see time_launches)
+_MARK = []
+
+
+def mark_timed_region():
+    """Launch a one-workgroup fa_probe_mfma right before the timed steps (outside the timed
+    events): in a rocprofv3 kernel trace it marks where each leg's timed dispatches start,
+    whatever the length of the time-based warm-up (rocprof_summary --after-marker)."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    if not _MARK:
+        _MARK.append(torch.empty((256,), dtype=torch.float32, device="cuda"))
+    sink = _MARK[0]
+    st = fa.library().fa_probe_mfma(sink.data_ptr(), sink.numel() * 4, 1, 1,
+                                    torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"marker launch failed: {fa.status_str(st)}")
 
 
 def time_launches(fn, steps: int, warmup: int, blocks: int = 5, warmup_s: float | None = None):
@@ -91,6 +107,7 @@ def time_launches(fn, steps: int, warmup: int, blocks: int = 5, warmup_s: float 
         torch.cuda.synchronize()
     LAST_WARMUP.clear()
     LAST_WARMUP.update({"steps": warmup + extra, "seconds": time.perf_counter() - t_w})
+    mark_timed_region()
     nb = max(1, min(blocks, steps))
     edges = [round(i * steps / nb) for i in range(nb + 1)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
@@ -373,6 +390,44 @@ def bwd_record(num: int, steps: int, warmup: int):
     return rec
 
 
+def bwd_bias_record(num: int, steps: int, warmup: int):
+    """fa_bwd_bias over workload `num` with its full [B, H, Nq, Nk] bias (as in the biased
+    prefill leg) and the seeded dO; o and lse from fa_fwd_bias (not timed); no dBias."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    w = W.WORKLOADS[num]
+    q, k, v = W.make_inputs(w, "cuda")
+    bias = W.make_bias(w, "cuda")
+    do = W.make_grad(w, "cuda")
+    o, lse = fa.fwd_bias(q, k, v, bias, scale=w.scale, causal=w.causal)
+    dq = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.B, w.H, w.Nk, w.d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = torch.empty((fa.bwd_workspace_bytes(w.B, w.H, w.Nq),), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.bwd_bias(q, k, v, bias, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                    workspace=ws)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    achieved = w.bwd_flops / (ev_ms * 1e-3) / 1e12
+    rec = {
+        "workload": f"{w.name}, plus a full [B, H, Nq, Nk] bias", "B": w.B, "H": w.H, "Nq": w.Nq,
+        "Nk": w.Nk, "d": w.d, "causal": w.causal, "flops_per_call": w.bwd_flops,
+        "flops_note": "the five contractions of the backward, as in the unbiased leg; both "
+                      "kernels also read the visible half of the bias",
+        "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "note": "kernel_ms spans the three launches of one call (statistics, dK/dV, dQ)",
+        "tflops": w.bwd_flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    del q, k, v, bias, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def decode_record(steps: int, warmup: int, cpu: bool = False):
     """fa_decode_splitkv on the decode workload; with cpu, also the oracle over every
     (b, h) of the same cache on the host's cores (cpu_baseline, full)."""
@@ -466,7 +521,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen", "fp8",
-                                       "bias"],
+                                       "bias", "backward_bias"],
                     default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
@@ -502,6 +557,10 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps({"backward": bwd_record(args.workload, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "backward_bias":
+        print(json.dumps({"backward_bias": bwd_bias_record(args.workload, args.steps, args.warmup)}),
+              flush=True)
         return
 
     main_rec, (w, q, k, v) = prefill_record(args.workload, args.steps, args.warmup)
@@ -577,6 +636,8 @@ def main():
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup), cpu=cpu)
         extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))
         extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
+        extra["backward_bias"] = bwd_bias_record(args.workload, max(5, args.steps // 2),
+                                                 max(2, args.warmup // 2))
         out["also"] = extra
     print(json.dumps(out), flush=True)
 

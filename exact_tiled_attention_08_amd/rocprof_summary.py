@@ -56,12 +56,36 @@ def counter_rows(db: str):
     return [dict(zip(cols, r)) for r in rows]
 
 
-def summarise(dbs, match: str | None, wgs: int | None = None, calls: tuple | None = None):
+MARKER = "mfma_probe_kernel"  # bench.py launches it with one workgroup right before timed steps
+
+
+def marker_ids(db: str):
+    """Dispatch ids of the one-workgroup probe launches that mark timed regions, in order."""
+    return sorted(did for name, _, grid, wg, *_, did in kernel_rows(db)
+                  if MARKER in name and grid // max(1, wg) == 1)
+
+
+def summarise(dbs, match: str | None, wgs: int | None = None, calls: tuple | None = None,
+              after: tuple | None = None):
     """calls=(a, b): keep only dispatches a .. b-1 of each kernel and launch shape, in
-    dispatch order (e.g. the timed launches after the warm-up ones)."""
+    dispatch order (e.g. the timed launches after the warm-up ones). after=(i, n): keep only
+    the first n dispatches of each kernel and launch shape that follow the i-th marker
+    launch and precede the next one (0-based; bench.py issues one right before each leg's
+    timed steps, after its warm-up, whose length depends on time)."""
     by = {}
+    lo, hi = {}, {}
+    if after is not None:
+        for db in dbs:
+            ids = marker_ids(db)
+            if len(ids) <= after[0]:
+                raise SystemExit(f"{db}: no marker launch number {after[0]}")
+            lo[db] = ids[after[0]]
+            hi[db] = ids[after[0] + 1] if after[0] + 1 < len(ids) else None
     for db in dbs:
         for name, dur, grid, wg, lds, vgpr, agpr, did in kernel_rows(db):
+            # the leg's dispatches: after its marker and before the next leg's
+            if after is not None and (did <= lo[db] or (hi[db] is not None and did >= hi[db])):
+                continue
             if match and match not in name:
                 continue
             if wgs is not None and grid // max(1, wg) != wgs:
@@ -74,6 +98,8 @@ def summarise(dbs, match: str | None, wgs: int | None = None, calls: tuple | Non
         ent["d"].sort()
         if calls is not None:
             ent["d"] = ent["d"][calls[0]:calls[1]]
+        if after is not None:
+            ent["d"] = ent["d"][:after[1]]
         ent["d"] = [dur for _, dur in ent["d"]]
     by = {k: e for k, e in by.items() if e["d"]}
     counters = {}
@@ -246,13 +272,21 @@ def main():
     ap.add_argument("--wgs", type=int, default=None, help="keep launches of this many workgroups")
     ap.add_argument("--calls", default=None,
                     help="A:B keeps dispatches A .. B-1 of each kernel, in dispatch order")
+    ap.add_argument("--after-marker", default=None,
+                    help="I:N keeps the first N dispatches of each kernel after the I-th marker "
+                         "launch (the timed steps of bench.py's I-th leg)")
     args = ap.parse_args()
     calls = tuple(int(x) for x in args.calls.split(":")) if args.calls else None
-    by, counters = summarise(args.dbs, args.match, args.wgs, calls)
+    after = tuple(int(x) for x in args.after_marker.split(":")) if args.after_marker else None
+    by, counters = summarise(args.dbs, args.match, args.wgs, calls, after)
     text = render(by, counters, args.command)
     if calls:
         text = text.replace("| kernel | calls |", f"Dispatches {calls[0]} .. {calls[1] - 1} of each kernel "
                             "(in dispatch order) only.\n\n| kernel | calls |", 1)
+    if after:
+        text = text.replace("| kernel | calls |", f"The {after[1]} dispatches of each kernel that follow "
+                            f"marker launch {after[0]} (the timed steps of that benchmark leg, after "
+                            "its warm-up) only.\n\n| kernel | calls |", 1)
     print(text)
 
 
