@@ -74,23 +74,21 @@ def test_worked_example_block_states():
         s = np.array(ex["scores"], np.float64)
         vals = np.array(ex["values"], np.float64)[:, None]
         B = ex["block_size"]
-        st = tm.State(1)
+        st = tm.empty(1, 1)
         for bi, blk in enumerate(ex["blocks"]):
             lo, hi = bi * B, (bi + 1) * B
+            loc = tm.of_keys(s[None, lo:hi], vals[lo:hi])
             if "local_l" in blk:
-                loc = tm.local_state(s[lo:hi], vals[lo:hi], 1)
-                for name, got in (("local_m", loc.m), ("local_l", loc.l), ("local_acc", loc.o[0])):
+                for name, got in (("local_m", loc.m[0]), ("local_l", loc.l[0]),
+                                  ("local_acc", loc.o[0, 0])):
                     val, tol = blk[name]
                     assert abs(got - val) <= tol + 1e-12, (key, name, got, val)
-                m_new = max(st.m, loc.m)
-                for name, got in (("scale_old", math.exp(st.m - m_new)),
-                                  ("scale_new", math.exp(loc.m - m_new))):
+                _, f_old, f_new = tm.factors(st, loc)
+                for name, got in (("scale_old", f_old[0]), ("scale_new", f_new[0])):
                     val, tol = blk[name]
                     assert abs(got - val) <= tol + 1e-12, (key, name, got, val)
-                st = tm.merge(st, loc)
-            else:
-                tm.update(st, s[lo:hi], vals[lo:hi])
-            for name, got in (("m", st.m), ("l", st.l), ("acc", st.o[0])):
+            st = tm.combine(st, loc)
+            for name, got in (("m", st.m[0]), ("l", st.l[0]), ("acc", st.o[0, 0])):
                 if name not in blk:
                     continue
                 val, tol = blk[name]
@@ -118,16 +116,17 @@ def test_worked_example_two_tiles_interview():
     # block states of the example, tile size 1
     s = np.array([_num(x) for x in ex["scores"]])
     vals = np.array(ex["values"])[:, None]
-    st = tm.State(1)
+    st = tm.empty(1, 1)
     for bi, blk in enumerate(ex["blocks"]):
-        m_old = st.m
-        tm.update(st, s[bi:bi + 1], vals[bi:bi + 1])
-        for name, got in (("m", st.m), ("l", st.l), ("o", st.o[0])):
+        loc = tm.of_keys(s[None, bi:bi + 1], vals[bi:bi + 1])
+        _, alpha, _ = tm.factors(st, loc)
+        st = tm.combine(st, loc)
+        for name, got in (("m", st.m[0]), ("l", st.l[0]), ("o", st.o[0, 0])):
             val, tol = blk[name]
             assert abs(got - _num(val)) <= tol + 1e-15, (name, got, val)
         if "alpha" in blk:
             val, tol = blk["alpha"]
-            assert abs(math.exp(m_old - st.m) - val) <= tol
+            assert abs(alpha[0] - val) <= tol
 
 
 # ---------------------------------------------------------------- closed forms
@@ -326,14 +325,12 @@ def test_prefix_property():
     q, k, v = _rand((1, 1, 3, d), rng), _rand((1, 1, nk, d), rng), _rand((1, 1, nk, d), rng)
     qh, kh, vh = _heads(q, k, v)[0]
     s = tm.scores(qh, kh, 0.4, False)
-    for i in range(3):
-        st = tm.State(d)
-        for j0 in range(0, nk, T):
-            tm.update(st, s[i, j0:j0 + T], vh[j0:j0 + T])
-            n = min(nk, j0 + T)
-            o, lse = oracle.attention(q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], 0.4)
-            fo, fl = tm.finish(st)
-            assert np.max(np.abs(fo - o[0])) <= 1e-13 and abs(fl - lse[0]) <= 1e-13
+    st = tm.empty(3, d)
+    for lo, hi in tm.bounds(nk, T):
+        st = tm.combine(st, tm.of_keys(s[:, lo:hi], vh[lo:hi]))
+        o, lse = oracle.attention(q, k[:, :, :hi], v[:, :, :hi], 0.4)
+        fo, fl = tm.finish(st)
+        assert np.max(np.abs(fo - o)) <= 1e-13 and np.max(np.abs(fl - lse)) <= 1e-13
 
 
 @pytest.mark.parametrize("splits", [1, 2, 7, 64])

@@ -1,91 +1,87 @@
-"""Float64 model of the tiled online-softmax recurrence (test helper, not the oracle).
+"""Float64 model of tiled attention built on one combine operation (test helper, not the oracle).
 
-The oracle evaluates the plain definition. This module evaluates the same
-result the way the kernels do: keys arrive in tiles, and each query row keeps
-a running state (m, l, o) that is rescaled whenever the running max rises.
-Agreement between the two (to float64 rounding) pins the oracle against an
-independent formulation, and the per-block states are compared with the
-intermediates the pages print.
+The oracle evaluates the plain definition. This module reaches the same result the way a
+tiled kernel does, with the keys taken a tile or a chunk at a time, so agreement between
+the two (to float64 rounding) pins the oracle against an independent formulation, and the
+intermediate states can be compared with the ones the pages print.
 
-- One-sided update of the running state by a new tile (running max m, running
-  sum of exponentials l, unnormalised weighted sum o, rescale factor
-  alpha = exp(m_old - m_new), divide by l after the last tile):
-  "FlashAttention: Attention Is Limited by Memory, Not Math", section "How
-  tiling and online softmax stay exact"; "Explain FlashAttention ...",
-  section "Keep only the state needed for the final weighted average".
-- Tiles whose scores are all masked are skipped, so the first real update
-  never evaluates -inf - (-inf); a row that saw no key returns zeros:
-  "Explain FlashAttention ...", section "Executable recurrence, with an
-  empty-state policy".
-- Two-sided merge of partial states computed against their own local maxima
-  (scale_old = exp(m_old - m_new), scale_new = exp(m_block - m_new)), which
-  returns a state of the same shape and therefore chains:
-  "Flash Attention Optimization", section "The fix: tile the computation,
-  never materialize the full matrix"; "Handwritten Notes on Flash
-  Attention", section "Merging two blocks".
+Everything here is a fold of one operation on partial results. The partial result of a
+query row over a set of keys is the triple (m, l, o): m the largest visible score, l the sum
+of exp(s - m) over the visible keys and o the same weights applied to the value rows. Two
+partials over disjoint key sets combine into the partial over their union by bringing both
+to the larger of the two maxima (factors exp(m_a - m) and exp(m_b - m)); a partial with no
+visible key (m = -inf, l = 0, o = 0) is the neutral element and takes factor 0, so -inf - -inf
+is never formed. The pages' two forms are both this combine:
+- the running update by a new tile, where the new tile's partial is taken against its own
+  max and combined into the running state ("FlashAttention: Attention Is Limited by Memory,
+  Not Math", section "How tiling and online softmax stay exact"; "Explain FlashAttention
+  ...", section "Keep only the state needed for the final weighted average"; a fully masked
+  tile is neutral, which is the empty-state policy of section "Executable recurrence, with
+  an empty-state policy");
+- the merge of chunk states computed against their own maxima ("Flash Attention
+  Optimization", section "The fix: tile the computation, never materialize the full
+  matrix"; "Handwritten Notes on Flash Attention", section "Merging two blocks").
+The result is o / l and LSE = m + ln l; a row that saw no key gives (0, -inf).
+
+All functions work on every query row of one head at once (arrays over rows).
 """
 from __future__ import annotations
 
 import math
+from typing import NamedTuple
 
 import numpy as np
 
 NEG_INF = -math.inf
 
 
-class State:
-    """Running (m, l, o) of one query row; o has the value dimension."""
-
-    def __init__(self, dv: int):
-        self.m = NEG_INF
-        self.l = 0.0
-        self.o = np.zeros(dv, np.float64)
-
-    def copy(self):
-        s = State(self.o.size)
-        s.m, s.l, s.o = self.m, self.l, self.o.copy()
-        return s
+class Partial(NamedTuple):
+    m: np.ndarray      # [rows] largest visible score, -inf if none
+    l: np.ndarray      # [rows] sum of exp(s - m)
+    o: np.ndarray      # [rows, dv] sum of exp(s - m) * v
 
 
-def update(state: State, s_tile: np.ndarray, v_tile: np.ndarray) -> State:
-    """Fold one tile of scores (-inf = masked) and its value rows into the state."""
-    tile_max = float(np.max(s_tile)) if s_tile.size else NEG_INF
-    if tile_max == NEG_INF:          # nothing visible in this tile: skip it
-        return state
-    m_new = max(state.m, tile_max)
-    alpha = 0.0 if state.m == NEG_INF else math.exp(state.m - m_new)
-    w = np.exp(s_tile - m_new)       # masked entries give exactly 0
-    state.l = alpha * state.l + float(w.sum())
-    state.o = alpha * state.o + w @ v_tile
-    state.m = m_new
-    return state
+def empty(rows: int, dv: int) -> Partial:
+    return Partial(np.full(rows, NEG_INF), np.zeros(rows), np.zeros((rows, dv)))
 
 
-def local_state(s_tile: np.ndarray, v_tile: np.ndarray, dv: int) -> State:
-    """A block's own state, relative to the block's own max (as in a split chunk)."""
-    return update(State(dv), s_tile, v_tile)
+def _finite_or_zero(x: np.ndarray) -> np.ndarray:
+    return np.where(np.isfinite(x), x, 0.0)
 
 
-def merge(a: State, b: State) -> State:
-    """Two-sided merge of two partial states; an empty state (m=-inf) is skipped."""
-    if b.m == NEG_INF:
-        return a.copy()
-    if a.m == NEG_INF:
-        return b.copy()
-    out = State(a.o.size)
-    out.m = max(a.m, b.m)
-    scale_old = math.exp(a.m - out.m)
-    scale_new = math.exp(b.m - out.m)
-    out.l = a.l * scale_old + b.l * scale_new
-    out.o = a.o * scale_old + b.o * scale_new
-    return out
+def of_keys(s: np.ndarray, v: np.ndarray) -> Partial:
+    """Partial over a block of keys: scores s [rows, n] (-inf = hidden), values v [n, dv],
+    taken against the block's own row maxima."""
+    rows, n = s.shape
+    if n == 0:
+        return empty(rows, v.shape[1])
+    m = s.max(axis=1)
+    w = np.exp(s - _finite_or_zero(m)[:, None])   # hidden scores give exactly 0
+    return Partial(m, w.sum(axis=1), w @ v)
 
 
-def finish(state: State):
-    """(output row, log-sum-exp) of a finished state; empty row -> (0, -inf)."""
-    if state.l == 0.0:
-        return np.zeros_like(state.o), NEG_INF
-    return state.o / state.l, state.m + math.log(state.l)
+def factors(a: Partial, b: Partial):
+    """The two factors that bring a and b to their common max (0 for an empty side)."""
+    m = np.maximum(a.m, b.m)
+    base = _finite_or_zero(m)
+    fa = np.where(np.isfinite(a.m), np.exp(_finite_or_zero(a.m) - base), 0.0)
+    fb = np.where(np.isfinite(b.m), np.exp(_finite_or_zero(b.m) - base), 0.0)
+    return m, fa, fb
+
+
+def combine(a: Partial, b: Partial) -> Partial:
+    """Partial over the union of the two disjoint key sets of a and b."""
+    m, fa, fb = factors(a, b)
+    return Partial(m, fa * a.l + fb * b.l, fa[:, None] * a.o + fb[:, None] * b.o)
+
+
+def finish(p: Partial):
+    """(output rows, log-sum-exp per row); rows that saw no key give (0, -inf)."""
+    seen = p.l > 0
+    l_safe = np.where(seen, p.l, 1.0)
+    o = np.where(seen[:, None], p.o / l_safe[:, None], 0.0)
+    lse = np.where(seen, p.m + np.log(l_safe), NEG_INF)
+    return o, lse
 
 
 def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
@@ -103,34 +99,31 @@ def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarr
     return s
 
 
+def bounds(nk: int, size: int):
+    """[lo, hi) of consecutive key blocks of ``size`` (the last may be short)."""
+    return [(lo, min(nk, lo + size)) for lo in range(0, nk, size)]
+
+
 def tiled_head(q, k, v, scale, causal, tile):
-    """Attention for one head by the one-sided recurrence over key tiles of size ``tile``."""
+    """Attention for one head, key tiles of ``tile`` folded left to right into a running
+    partial."""
     s = scores(q, k, scale, causal)
-    nq, nk = s.shape
-    o = np.zeros((nq, v.shape[1]))
-    lse = np.zeros(nq)
-    for i in range(nq):
-        st = State(v.shape[1])
-        for j0 in range(0, nk, tile):
-            update(st, s[i, j0:j0 + tile], v[j0:j0 + tile])
-        o[i], lse[i] = finish(st)
-    return o, lse
+    acc = empty(s.shape[0], v.shape[1])
+    for lo, hi in bounds(s.shape[1], tile):
+        acc = combine(acc, of_keys(s[:, lo:hi], v[lo:hi]))
+    return finish(acc)
 
 
 def split_merge_head(q, k, v, scale, causal, num_splits):
-    """Attention for one head by splitting keys into chunks of ceil(Nk/S) and merging."""
+    """Attention for one head with the keys split into num_splits chunks of ceil(Nk/S)
+    (trailing chunks may be short or empty), one partial per chunk, merged afterwards by a
+    balanced tree of combines (a different association than the running fold)."""
     s = scores(q, k, scale, causal)
-    nq, nk = s.shape
+    nk = s.shape[1]
     chunk = -(-nk // num_splits)
-    o = np.zeros((nq, v.shape[1]))
-    lse = np.zeros(nq)
-    for i in range(nq):
-        parts = []
-        for c in range(num_splits):
-            lo, hi = c * chunk, min(nk, (c + 1) * chunk)
-            parts.append(local_state(s[i, lo:hi], v[lo:hi], v.shape[1]))
-        acc = State(v.shape[1])
-        for p in parts:
-            acc = merge(acc, p)
-        o[i], lse[i] = finish(acc)
-    return o, lse
+    parts = [of_keys(s[:, c * chunk:min(nk, (c + 1) * chunk)], v[c * chunk:min(nk, (c + 1) * chunk)])
+             for c in range(num_splits)]
+    while len(parts) > 1:
+        parts = [combine(parts[i], parts[i + 1]) if i + 1 < len(parts) else parts[i]
+                 for i in range(0, len(parts), 2)]
+    return finish(parts[0])
