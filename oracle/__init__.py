@@ -352,3 +352,40 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         o[cq[b]:cq[b + 1]] = ob.reshape(H, nq, d).transpose(1, 0, 2)
         lse[:, cq[b]:cq[b + 1]] = lb.reshape(H, nq)
     return o, lse
+
+
+def attention_varlen_bwd(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale: float,
+                         causal: bool = False, threads: int | None = None):
+    """Float64 gradients of sum(O * dO) for O = attention_varlen(q, k, v, ...).
+
+    q, do [total_q, H, d]; k, v [total_k, H, d] (float32 or bfloat16, CPU), with the
+    sequence offsets and the in-sequence mask of ``attention_varlen``. The sequences share no
+    scores, so the gradients are those of ``attention_bwd`` on each sequence's slice (the
+    chain rule of "Explain FlashAttention ...", section "Exact attention, finite precision
+    and backward", applied per sequence). Returns (dq [total_q, H, d], dk [total_k, H, d],
+    dv [total_k, H, d]) float64; rows of a sequence with no query rows or no keys are zero.
+    """
+    total_q, H, d = q.shape
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or cq[0] != 0 or ck[0] != 0 or cq[-1] != total_q or ck[-1] != k.shape[0]:
+        raise ValueError("cu_seqlens must start at 0 and end at the packed lengths")
+    if do.shape != q.shape or v.shape != k.shape:
+        raise ValueError("do must match q and v must match k")
+    dq = np.zeros((total_q, H, d), np.float64)
+    dk = np.zeros((k.shape[0], H, d), np.float64)
+    dv = np.zeros((k.shape[0], H, d), np.float64)
+    for b in range(len(cq) - 1):
+        nq, nk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        if nq < 0 or nk < 0:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        if nq == 0 or nk == 0:
+            continue  # nothing attends: every gradient of the sequence is zero
+        sl = lambda t, lo, hi: t[lo:hi].permute(1, 0, 2)[None].contiguous()   # [1, H, n, d]
+        gq, gk, gv = attention_bwd(sl(q, cq[b], cq[b + 1]), sl(k, ck[b], ck[b + 1]),
+                                   sl(v, ck[b], ck[b + 1]), sl(do, cq[b], cq[b + 1]),
+                                   scale, causal, threads=threads)
+        dq[cq[b]:cq[b + 1]] = gq.reshape(H, nq, d).transpose(1, 0, 2)
+        dk[ck[b]:ck[b + 1]] = gk.reshape(H, nk, d).transpose(1, 0, 2)
+        dv[ck[b]:ck[b + 1]] = gv.reshape(H, nk, d).transpose(1, 0, 2)
+    return dq, dk, dv
