@@ -40,7 +40,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_bias", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv",
            "fa_decode_splitkv_noalloc", "fa_decode_paged",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_bias", "fa_probe_mfma", "fa_status_str", "fa_last_hip_error",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_varlen", "fa_bwd_bias", "fa_probe_mfma", "fa_status_str", "fa_last_hip_error",
            "fa_last_hip_error_str")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -59,6 +59,8 @@ _SIGS = {
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _sz, _i, _vp]),
+    "fa_bwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                           _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
     "fa_bwd_bias": (_i, [_vp, _vp, _vp, _vp, ctypes.c_longlong, ctypes.c_longlong, ctypes.c_longlong,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
                          _i, _vp]),
@@ -483,6 +485,52 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, d
         _causal_arg(causal), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _dtype_code(q), _stream_ptr(q.device))
     _raise(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+               max_seqlen_k: int, scale: float | None = None, causal: bool = False, dq=None,
+               dk=None, dv=None, workspace=None):
+    """Backward of fwd_varlen: (dq [total_q, H, d], dk, dv [total_k, H, d]) float32, given the
+    (o, lse) that fwd_varlen returned for the same packed inputs and offsets."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[1:] != q.shape[1:] \
+            or do.shape != q.shape:
+        raise ValueError("q, do must be [total_q, H, d] and k, v [total_k, H, d]")
+    if not (q.dtype == k.dtype == v.dtype == do.dtype):
+        raise ValueError("q, k, v and do must share one dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 \
+            or cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [B + 1]")
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    B = cu_seqlens_q.numel() - 1
+    if len({t.device for t in (q, k, v, do, cu_seqlens_q, cu_seqlens_k)}) != 1:
+        raise ValueError("q, k, v, do and the sequence offsets must be on one device")
+    if not isinstance(o, torch.Tensor) or o.shape != q.shape or o.dtype != torch.float32 \
+            or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be the contiguous float32 [total_q, H, d] output of fwd_varlen")
+    if not isinstance(lse, torch.Tensor) or lse.shape != (H, total_q) or lse.dtype != torch.float32 \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be the contiguous float32 [H, total_q] output of fwd_varlen")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = _out_arg(dq, (total_q, H, d), q.device, "dq")
+    dk = _out_arg(dk, (total_k, H, d), q.device, "dk")
+    dv = _out_arg(dv, (total_k, H, d), q.device, "dv")
+    workspace = _workspace_arg(workspace, bwd_workspace_bytes(B, H, max(1, int(max_seqlen_q))),
+                               q.device)
+    st = library().fa_bwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), B, H, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d,
+        float(scale), _causal_arg(causal), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _dtype_code(q), _stream_ptr(q.device))
+    _raise(st, "fa_bwd_varlen")
     return dq, dk, dv
 
 

@@ -400,6 +400,71 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   return finish_launch(fa::launch_bwd(p, d, causal != 0, (hipStream_t)stream));
 }
 
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes,
+                        fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens_q ||
+      !cu_seqlens_k)
+    return FA_ERR_NULL;
+  if (B < 1 || H < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
+      d < 1)
+    return FA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX || (long long)total_q * H * d > (1LL << 62) / 4 ||
+      (long long)total_k * H * d > (1LL << 62) / 4)
+    return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // a tile's rows must lie within 2^31 bytes of its first row (32-bit load offsets)
+  if ((long long)H * d * 2 * 128 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale) || causal < 0 || causal > 2) return FA_ERR_VALUE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, max_seqlen_q);
+  if (!workspace || need == 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)cu_seqlens_q & 3u) != 0 ||
+      ((uintptr_t)cu_seqlens_k & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const long long nkt = (max_seqlen_k + fa::kBwdKeyRows - 1) / fa::kBwdKeyRows;
+  const long long nqt = (max_seqlen_q + fa::kBwdQueryRows - 1) / fa::kBwdQueryRows;
+  if (BH * nkt > INT32_MAX || BH * nqt > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws = (float*)workspace;
+  p.BH = (int)BH;
+  p.Nq = max_seqlen_q;
+  p.Nk = max_seqlen_k;
+  p.Nq_pad = (int)(nqt * fa::kBwdQueryRows);
+  p.nkt = (int)nkt;
+  p.nqt = (int)nqt;
+  // one (b, h) pair per XCD group, as in the forward over packed batches
+  p.hpg_kv = 1;
+  p.hpg_q = 1;
+  p.scale = scale;
+  p.c = scale * fa::kLog2e;
+  p.H = H;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.B = B;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.top_left = causal == 2;
+  (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
+  return finish_launch(fa::launch_bwd_varlen(p, d, causal != 0, (hipStream_t)stream));
+}
+
 fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
                       long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
                       const float* o, const float* lse, const void* dout, float* dq, float* dk,

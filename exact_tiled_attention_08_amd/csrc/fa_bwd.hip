@@ -114,9 +114,46 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // Offset of the statistics of query row i inside one head's workspace block.
 __device__ __forceinline__ int stat_index(int i) { return (i >> 6) * 128 + (i & 63); }
 
+// The rows of pair bh. Dense: (b, h) of [B][H][N][d] tensors, row stride d. VARLEN: pair
+// bh = h*B + b is sequence b of head h in the packed [total][H][d] tensors, row stride H*d,
+// its row counts from the offsets (clamped into the tensors, then to the caps Nq and Nk of
+// the launch: rows past a cap are not computed) and its causal offset from its own counts.
+struct PairView {
+  int Nq, Nk, off;
+  long long qbase, kbase;  // element offset of row 0 on the query side and the key side
+  int rs;                  // elements between consecutive rows
+  long long lbase;         // index of row 0's LSE
+};
+template <int D, bool VARLEN>
+__device__ __forceinline__ PairView pair_view(const BwdParams& p, int bh) {
+  PairView v;
+  if constexpr (VARLEN) {
+    const int h = bh / p.B;
+    const int b = bh - h * p.B;
+    const int qs = min(max(p.cu_q[b], 0), p.total_q);
+    const int ks = min(max(p.cu_k[b], 0), p.total_k);
+    v.Nq = min(min(max(p.cu_q[b + 1], qs), p.total_q) - qs, p.Nq);
+    v.Nk = min(min(max(p.cu_k[b + 1], ks), p.total_k) - ks, p.Nk);
+    v.off = p.top_left ? 0 : v.Nk - v.Nq;
+    v.qbase = ((long long)qs * p.H + h) * D;
+    v.kbase = ((long long)ks * p.H + h) * D;
+    v.rs = p.H * D;
+    v.lbase = (long long)h * p.total_q + qs;
+  } else {
+    v.Nq = p.Nq;
+    v.Nk = p.Nk;
+    v.off = p.off;
+    v.qbase = (long long)bh * p.Nq * D;
+    v.kbase = (long long)bh * p.Nk * D;
+    v.rs = D;
+    v.lbase = (long long)bh * p.Nq;
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------- row statistics
 
-template <int D>
+template <int D, bool VARLEN = false>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int TPR = D / 8;         // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;     // rows per block
@@ -128,8 +165,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const int i = (int)(row - (long long)bh * p.Nq_pad);
   float acc = 0.f;
   float l2 = INFINITY;
-  if (row < total && i < p.Nq) {
-    const size_t e = ((size_t)bh * p.Nq + i) * D + 8 * part;
+  const PairView pv = pair_view<D, VARLEN>(p, row < total ? bh : 0);
+  if (row < total && i < pv.Nq) {
+    const size_t e = (size_t)(pv.qbase + (long long)i * pv.rs) + 8 * part;
     const bf16x8 dov = *(const bf16x8*)((const __bf16*)p.dout + e);
     const f32x4 o0 = *(const f32x4*)(p.o + e);
     const f32x4 o1 = *(const f32x4*)(p.o + e + 4);
@@ -138,7 +176,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
       acc = __builtin_fmaf((float)dov[t], o0[t], acc);
       acc = __builtin_fmaf((float)dov[4 + t], o1[t], acc);
     }
-    const float L = p.lse[(size_t)bh * p.Nq + i];
+    const float L = p.lse[pv.lbase + i];
     l2 = (L == -INFINITY) ? INFINITY : L * kLog2e;
   }
 #pragma unroll
@@ -156,13 +194,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // per query tile as a [64 query][128 key] bfloat16 tile next to Q and dO, with the same
 // 256-byte-row swizzle, and read per lane (one key, 16 queries per step) with the same
 // transpose reads as Q^T. DBIAS: dS, the gradient of a full bias, is also written out.
-template <int D, bool CAUSAL, bool BIAS = false, bool DBIAS = false>
+template <int D, bool CAUSAL, bool BIAS = false, bool DBIAS = false, bool VARLEN = false>
 __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   using C = BCfg<D>;
   constexpr int BTILE = kRows * 2 * kBwdKeyRows;             // bias tile, 256-byte rows
   constexpr int BOFF = 2 * C::TILEB + 512;                    // its offset inside a stage
   constexpr int STAGE = BOFF + (BIAS ? BTILE : 0);  // Q tile, dO tile, 64 LSE2 + 64 D, bias
   static_assert(!DBIAS || BIAS, "the bias gradient needs the biased scores");
+  static_assert(!(BIAS && VARLEN), "the bias is offered for dense batches only");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -177,11 +216,14 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int k0 = kt * kBwdKeyRows;
   const int kw0 = k0 + 32 * w;  // first key of this wave
   const int key = kw0 + col;    // this lane's key
+  const PairView pv = pair_view<D, VARLEN>(p, bh);
+  const int Nq = pv.Nq, Nk = pv.Nk, off = pv.off, rs = pv.rs;
+  if (VARLEN && k0 >= Nk) return;  // the whole workgroup: this sequence has no such keys
 
-  const __bf16* __restrict__ qh = (const __bf16*)p.q + (size_t)bh * p.Nq * D;
-  const __bf16* __restrict__ doh = (const __bf16*)p.dout + (size_t)bh * p.Nq * D;
-  const __bf16* __restrict__ kh = (const __bf16*)p.k + (size_t)bh * p.Nk * D;
-  const __bf16* __restrict__ vh = (const __bf16*)p.v + (size_t)bh * p.Nk * D;
+  const __bf16* __restrict__ qh = (const __bf16*)p.q + pv.qbase;
+  const __bf16* __restrict__ doh = (const __bf16*)p.dout + pv.qbase;
+  const __bf16* __restrict__ kh = (const __bf16*)p.k + pv.kbase;
+  const __bf16* __restrict__ vh = (const __bf16*)p.v + pv.kbase;
   const float* __restrict__ wsh = p.ws + (size_t)bh * p.Nq_pad * 2;
   // bias of (b, h), query 0, key k0 (BIAS only)
   const uint16_t* biasw = nullptr;
@@ -195,9 +237,9 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    if (key < p.Nk) {
-      kf[kk] = *(const bf16x8*)(kh + (size_t)key * D + 16 * kk + 8 * g);
-      vf[kk] = *(const bf16x8*)(vh + (size_t)key * D + 16 * kk + 8 * g);
+    if (key < Nk) {
+      kf[kk] = *(const bf16x8*)(kh + (size_t)key * rs + 16 * kk + 8 * g);
+      vf[kk] = *(const bf16x8*)(vh + (size_t)key * rs + 16 * kk + 8 * g);
     } else {
       kf[kk] = bf16x8{};
       vf[kk] = bf16x8{};
@@ -206,9 +248,9 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // Query tiles to visit: under the causal mask query i sees key j iff j <= i + off, so
   // the first query that sees key k0 is k0 - off.
-  const int q_begin = CAUSAL ? max(0, k0 - p.off) : 0;
+  const int q_begin = CAUSAL ? max(0, k0 - off) : 0;
   const int t0 = q_begin / kRows;
-  const int t1 = (p.Nq + kRows - 1) / kRows;
+  const int t1 = (Nq + kRows - 1) / kRows;
 
   // Direct loads: slot s = n*kT + tid holds chunk position s % CHR of tile row s / CHR; the
   // swizzle depends only on row bits that repeat every ROWSTEP rows.
@@ -219,22 +261,22 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int r0 = t * kRows;
 #pragma unroll
     for (int n = 0; n < C::LOADS; ++n) {
-      const int row = min(lrow + n * C::ROWSTEP, p.Nq - 1 - r0);  // rows past Nq repeat row Nq-1
-      const uint32_t off = (uint32_t)(row * C::ROWB) + lchunk;
+      const int row = min(lrow + n * C::ROWSTEP, Nq - 1 - r0);  // rows past Nq repeat row Nq-1
+      const uint32_t loff = (uint32_t)(row * rs * 2) + lchunk;
       const uint32_t dst = (uint32_t)((n * kT + 64 * w) * 16);
-      dma16(qh + (size_t)r0 * D, off, lds_addr(st + dst));
-      dma16(doh + (size_t)r0 * D, off, lds_addr(st + C::TILEB + dst));
+      dma16(qh + (size_t)r0 * rs, loff, lds_addr(st + dst));
+      dma16(doh + (size_t)r0 * rs, loff, lds_addr(st + C::TILEB + dst));
     }
     if constexpr (BIAS) {
       // 64 rows x 16 chunks: slot n*kT + tid is row tid/16 + 16n at chunk position tid%16,
       // holding chunk (position ^ swizzle); rows past Nq repeat row Nq-1 and chunks at or
       // past Nk the chunk of key Nk-1 (their pairs are masked or not stored)
       const int brow = tid >> 4;
-      const int bch = min((tid & 15) ^ bswz<16>(brow), (p.Nk - 1 - k0) >> 3);
+      const int bch = min((tid & 15) ^ bswz<16>(brow), (Nk - 1 - k0) >> 3);
       const char* base = (const char*)(biasw + (size_t)r0 * p.bsq);
       const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(st + BOFF + 64 * w * 16));
       [&]<int... N>(std::integer_sequence<int, N...>) {
-        ((dma16(base, (uint32_t)(((long long)min(brow + 16 * N, p.Nq - 1 - r0) * p.bsq + 8 * bch) * 2),
+        ((dma16(base, (uint32_t)(((long long)min(brow + 16 * N, Nq - 1 - r0) * p.bsq + 8 * bch) * 2),
                 lbase + N * kT * 16)), ...);
       }(std::make_integer_sequence<int, BTILE / (16 * kT)>{});
     }
@@ -315,7 +357,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
         const float ds = pe * sd_t[b][e % EPM];
         dsb[x][e >> 3][e & 7] = (__bf16)ds;
         const int qi = qa0 + 32 * x + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (qi < p.Nq && key < p.Nk) p.dbias[((size_t)bh * p.Nq + qi) * p.Nk + key] = ds;
+        if (qi < Nq && key < Nk) p.dbias[((size_t)bh * Nq + qi) * Nk + key] = ds;
       } else {
         dsb[x][e >> 3][e & 7] = (__bf16)(pe * sd_t[b][e % EPM]);
       }
@@ -372,20 +414,20 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto zero_dbias = [&](int r_begin, int r_end) {
     const int kq = kw0 + 4 * (lane & 7);
     for (int r = r_begin + (lane >> 3); r < r_end; r += 8) {
-      float* row = p.dbias + ((size_t)bh * p.Nq + r) * p.Nk;
-      if (kq + 3 < p.Nk && ((p.Nk & 3) == 0)) {
+      float* row = p.dbias + ((size_t)bh * Nq + r) * Nk;
+      if (kq + 3 < Nk && ((Nk & 3) == 0)) {
         *(f32x4*)(row + kq) = f32x4{};
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (kq + u < p.Nk) row[kq + u] = 0.f;
+          if (kq + u < Nk) row[kq + u] = 0.f;
       }
     }
   };
 
   // Tiles before tm hold a query that misses a key of this workgroup (causal): they take
   // the masked stream; from tm on every pair is visible and the stream has no mask.
-  const int tm = CAUSAL ? min(t1, max(t0, (k0 + kBwdKeyRows - 1 - p.off + kRows - 1) / kRows)) : t0;
+  const int tm = CAUSAL ? min(t1, max(t0, (k0 + kBwdKeyRows - 1 - off + kRows - 1) / kRows)) : t0;
   auto body = [&](int t, auto maskedc) {
     constexpr bool MASKED = decltype(maskedc)::value;
     const int cur = (t - t0) & 1;
@@ -399,8 +441,8 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     f32x16 sinit[2] = {f32x16{}, f32x16{}};
     if constexpr (MASKED) {
       // no query of this tile sees a key of this wave: nothing to add (dS = 0 there)
-      if (qa0 + kRows - 1 + p.off < kw0) {
-        if constexpr (DBIAS) zero_dbias(qa0, min(qa0 + kRows, p.Nq));
+      if (qa0 + kRows - 1 + off < kw0) {
+        if constexpr (DBIAS) zero_dbias(qa0, min(qa0 + kRows, Nq));
         return;
       }
       // Masked pairs enter as S = -inf through the initial accumulator of the S product, so
@@ -409,7 +451,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
       // Query rows past Nq need no mask: their LSE2 is +inf.
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int lim = key - p.off - qa0 - 32 * x - 4 * g;  // visible iff 8(e/4) + e%4 >= lim
+        const int lim = key - off - qa0 - 32 * x - 4 * g;  // visible iff 8(e/4) + e%4 >= lim
 #pragma unroll
         for (int e = 0; e < 16; ++e) sinit[x][e] = (8 * (e >> 2) + (e & 3) < lim) ? -INFINITY : 0.f;
       }
@@ -428,7 +470,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   wait_loads();
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
-  if constexpr (DBIAS && CAUSAL) zero_dbias(0, min(t0 * kRows, p.Nq));  // tiles not visited
+  if constexpr (DBIAS && CAUSAL) zero_dbias(0, min(t0 * kRows, Nq));  // tiles not visited
   int t = t0;
   for (; t < tm; ++t) {
     body(t, std::true_type{});
@@ -440,9 +482,9 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4.
-  if (key < p.Nk) {
-    float* dkr = p.dk + ((size_t)bh * p.Nk + key) * D;
-    float* dvr = p.dv + ((size_t)bh * p.Nk + key) * D;
+  if (key < Nk) {
+    float* dkr = p.dk + pv.kbase + (size_t)key * rs;
+    float* dvr = p.dv + pv.kbase + (size_t)key * rs;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -466,7 +508,7 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
 // loads issued right after the tile's barrier, and reads 4 keys per 8-byte read in the
 // S^T layout (one query per lane column); 16-byte chunks are XOR-swizzled by (row / 2) % 8
 // against bank conflicts (as in the biased prefill).
-template <int D, bool CAUSAL, bool BIAS = false>
+template <int D, bool CAUSAL, bool BIAS = false, bool VARLEN = false>
 __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   using C = BCfg<D>;
   constexpr int STAGE = 2 * C::TILEB;  // K tile, V tile
@@ -485,20 +527,24 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   const int q0 = qt * kBwdQueryRows;
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + col;
+  static_assert(!(BIAS && VARLEN), "the bias is offered for dense batches only");
+  const PairView pv = pair_view<D, VARLEN>(p, bh);
+  const int Nq = pv.Nq, Nk = pv.Nk, off = pv.off, rs = pv.rs;
+  if (VARLEN && q0 >= Nq) return;  // the whole workgroup: this sequence has no such rows
 
-  const __bf16* __restrict__ qh = (const __bf16*)p.q + (size_t)bh * p.Nq * D;
-  const __bf16* __restrict__ doh = (const __bf16*)p.dout + (size_t)bh * p.Nq * D;
-  const __bf16* __restrict__ kh = (const __bf16*)p.k + (size_t)bh * p.Nk * D;
-  const __bf16* __restrict__ vh = (const __bf16*)p.v + (size_t)bh * p.Nk * D;
+  const __bf16* __restrict__ qh = (const __bf16*)p.q + pv.qbase;
+  const __bf16* __restrict__ doh = (const __bf16*)p.dout + pv.qbase;
+  const __bf16* __restrict__ kh = (const __bf16*)p.k + pv.kbase;
+  const __bf16* __restrict__ vh = (const __bf16*)p.v + pv.kbase;
   const float* __restrict__ wsh = p.ws + (size_t)bh * p.Nq_pad * 2;
 
   // Q and dO rows of this lane's query: B operands of S^T = K Q^T and dP^T = V dO^T.
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    if (qrow < p.Nq) {
-      qf[kk] = *(const bf16x8*)(qh + (size_t)qrow * D + 16 * kk + 8 * g);
-      df[kk] = *(const bf16x8*)(doh + (size_t)qrow * D + 16 * kk + 8 * g);
+    if (qrow < Nq) {
+      qf[kk] = *(const bf16x8*)(qh + (size_t)qrow * rs + 16 * kk + 8 * g);
+      df[kk] = *(const bf16x8*)(doh + (size_t)qrow * rs + 16 * kk + 8 * g);
     } else {
       qf[kk] = bf16x8{};
       df[kk] = bf16x8{};
@@ -515,12 +561,12 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]), "+v"(df[kk]));
   asm volatile("" : "+v"(lse2), "+v"(dsum));
 
-  int kv_end = p.Nk;
-  int wave_kv_end = (wq0 < p.Nq) ? p.Nk : 0;
+  int kv_end = Nk;
+  int wave_kv_end = (wq0 < Nq) ? Nk : 0;
   if (CAUSAL) {
-    const int last_q = min(q0 + kBwdQueryRows, p.Nq) - 1;
-    kv_end = min(p.Nk, last_q + p.off + 1);
-    if (wq0 < p.Nq) wave_kv_end = min(p.Nk, min(wq0 + 31, p.Nq - 1) + p.off + 1);
+    const int last_q = min(q0 + kBwdQueryRows, Nq) - 1;
+    kv_end = min(Nk, last_q + off + 1);
+    if (wq0 < Nq) wave_kv_end = min(Nk, min(wq0 + 31, Nq - 1) + off + 1);
   }
   const int ntiles = kv_end > 0 ? (kv_end + kRows - 1) / kRows : 0;
 
@@ -531,11 +577,11 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
     const int r0 = t * kRows;
 #pragma unroll
     for (int n = 0; n < C::LOADS; ++n) {
-      const int row = min(lrow + n * C::ROWSTEP, p.Nk - 1 - r0);  // rows past Nk repeat row Nk-1
-      const uint32_t off = (uint32_t)(row * C::ROWB) + lchunk;
+      const int row = min(lrow + n * C::ROWSTEP, Nk - 1 - r0);  // rows past Nk repeat row Nk-1
+      const uint32_t loff = (uint32_t)(row * rs * 2) + lchunk;
       const uint32_t dst = (uint32_t)((n * kT + 64 * w) * 16);
-      dma16(kh + (size_t)r0 * D, off, lds_addr(st + dst));
-      dma16(vh + (size_t)r0 * D, off, lds_addr(st + C::TILEB + dst));
+      dma16(kh + (size_t)r0 * rs, loff, lds_addr(st + dst));
+      dma16(vh + (size_t)r0 * rs, loff, lds_addr(st + C::TILEB + dst));
     }
   };
 
@@ -547,29 +593,29 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   uint32_t boff[4];
   if constexpr (BIAS) {
     const int b = bh / p.H;
-    const int r0 = min(wq0, p.Nq - 1);
+    const int r0 = min(wq0, Nq - 1);
     bwv = (const uint16_t*)p.bias + (size_t)b * p.bsb + (size_t)(bh - b * p.H) * p.bsh + (size_t)r0 * p.bsq;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int r = 8 * n + (lane >> 3);
-      const int dr = min(wq0 + r, p.Nq - 1) - r0;
+      const int dr = min(wq0 + r, Nq - 1) - r0;
       boff[n] = (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
     }
   }
   auto bias_issue = [&](int t) {
     const int ka = t * kRows;
     const char* base = (const char*)(bwv + ka);
-    if (ka + kRows <= p.Nk) {
+    if (ka + kRows <= Nk) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) dma16(base, boff[n], lds_addr(bwl + n * 64 * 16));
       return;
     }
     // the key tail: chunks at or past Nk take the chunk of key Nk-1 (masked anyway)
-    const int cmax = (p.Nk - 1 - ka) >> 3;
+    const int cmax = (Nk - 1 - ka) >> 3;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int r = 8 * n + (lane >> 3);
-      const int dr = min(wq0 + r, p.Nq - 1) - min(wq0, p.Nq - 1);
+      const int dr = min(wq0 + r, Nq - 1) - min(wq0, Nq - 1);
       const int ch = min((lane & 7) ^ ((r >> 1) & 7), cmax);
       const uint32_t off = (uint32_t)((long long)dr * p.bsq * 2) + 16u * (uint32_t)ch;
       dma16(base, off, lds_addr(bwl + n * 64 * 16));
@@ -601,8 +647,8 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
         dp = mfma(rfrag<D>(Vs, 32 * kb + col, 2 * kk + g), df[kk], dp);
       }
       // element i: key ka + 8(i/4) + 4g + i%4, query qrow
-      const bool need_mask = (ka + 32 > p.Nk) || (CAUSAL && ka + 31 > wq0 + p.off);
-      const int lim = (CAUSAL ? min(p.Nk - 1, qrow + p.off) : p.Nk - 1) - ka - 4 * g;
+      const bool need_mask = (ka + 32 > Nk) || (CAUSAL && ka + 31 > wq0 + off);
+      const int lim = (CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1) - ka - 4 * g;
       if constexpr (BIAS) {
         // s <- s * scale + bias, in natural-log units; keys ka + 8q + 4g + 0..3 sit at byte
         // 8g of chunk position (4kb + q) ^ ((col / 2) % 8) of this lane's row
@@ -638,8 +684,8 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   }
 
   // dQ^T: lane column = query, element i = dim 32db + 8(i/4) + 4g + i%4.
-  if (qrow < p.Nq) {
-    float* dqr = p.dq + ((size_t)bh * p.Nq + qrow) * D;
+  if (qrow < Nq) {
+    float* dqr = p.dq + pv.qbase + (size_t)qrow * rs;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -685,7 +731,31 @@ hipError_t launch(const BwdParams& prm, bool causal, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_varlen(const BwdParams& prm, bool causal, hipStream_t s) {
+  BwdParams p = prm;
+  constexpr int RPB = 256 / (D / 8);
+  const long long rows = (long long)p.BH * p.Nq_pad;
+  hipLaunchKernelGGL((bwd_pre_kernel<D, true>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned nkv = (unsigned)(p.BH * p.nkt), nq = (unsigned)(p.BH * p.nqt);
+  if (causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, false, true>), dim3(nkv), dim3(kT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, true>), dim3(nq), dim3(kT), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, false, true>), dim3(nkv), dim3(kT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, true>), dim3(nq), dim3(kT), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_varlen(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return launch_varlen<128>(p, causal, s);
+  return launch_varlen<64>(p, causal, s);
+}
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
   if (d == 128) return launch<128>(p, causal, s);

@@ -107,6 +107,17 @@ struct BwdParams {
   long long bsq;
   int H;
   float* dbias;
+  // Variable-length batches only (the backward of fa_fwd_varlen): q, dout, o, dq are packed
+  // [total_q][H][d] and k, v, dk, dv [total_k][H][d]; lse is [H][total_q]. Pair bh = h*B + b
+  // is sequence b of head h (cu_q, cu_k: B+1 device offsets, clamped into the tensors);
+  // Nq and Nk above are the caps max_seqlen_q and max_seqlen_k, and every pair's workspace
+  // block holds Nq_pad rows. top_left: causal alignment 2.
+  const int* cu_q;
+  const int* cu_k;
+  int B;
+  int total_q;
+  int total_k;
+  int top_left;
 };
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence would also wait
@@ -175,6 +186,7 @@ hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStrea
 hipError_t decode_scratch(int device, void** ptr);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_bias(const BwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_varlen(const BwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 // Query rows per workgroup of each prefill kernel (host needs it for the grid).

@@ -252,6 +252,35 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
                  fa_dtype dtype, void* stream);
 
 /*
+ * fa_bwd_varlen — fa_bwd for a packed batch of variable-length sequences: the gradients of
+ * a loss L with respect to q, k and v, given do = dL/dO and the o and lse that
+ * fa_fwd_varlen returned for the same inputs, offsets, scale and causal. Sequences share
+ * no scores, so each sequence's gradients are those of fa_bwd on its own rows ("Explain
+ * FlashAttention ...", section "Exact attention, finite precision and backward": the
+ * backward covers the masks and awkward dimensions the forward supports).
+ *   q, do [total_q][H][d]  FA_BF16     k, v [total_k][H][d]  FA_BF16
+ *   o     [total_q][H][d]  float32     lse  [H][total_q] float32 (as fa_fwd_varlen writes it)
+ *   dq    [total_q][H][d]  float32, dk, dv [total_k][H][d] float32 (written; every row of a
+ *   sequence within the caps below, zero where a row attends to nothing or is attended by
+ *   nothing)
+ *   cu_seqlens_q, cu_seqlens_k [B+1] int32 (device), causal 0, 1 or 2: as in fa_fwd_varlen.
+ *   max_seqlen_q, max_seqlen_k: upper bounds on every sequence's query and key counts (rows
+ *   past them are neither read nor written). Offsets outside [0, total] are clamped on the
+ *   device, so malformed ones cannot read or write outside the tensors.
+ *   workspace: at least fa_bwd_workspace_bytes(B, H, max_seqlen_q) bytes, 16-byte aligned,
+ *   owned by the caller; contents on entry are ignored, on return unspecified.
+ *   d in {64, 128}; H*d*256 < 2^31; scale finite and > 0. FA_F32 returns
+ *   FA_ERR_UNSUPPORTED. Three kernels on `stream`, every output element written once, as in
+ *   fa_bwd (deterministic).
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                        int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes,
+                        fa_dtype dtype, void* stream);
+
+/*
  * fa_bwd_bias — fa_bwd for the attention of fa_fwd_bias (S = scale * Q K^T + bias): the
  * gradients with respect to q, k and v of a loss L, given do = dL/dO and the o and lse
  * that fa_fwd_bias returned for the same q, k, v, bias, scale and causal; optionally also

@@ -216,6 +216,35 @@ def test_varlen_rejects(kw, status):
     assert _varlen(**kw) == status
 
 
+def _bwd_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cq=P, ck=P, B=2, H=4, tq=100,
+             tk=120, maxq=60, maxk=70, d=128, scale=0.1, causal=1, ws=P,
+             wsb=fa.bwd_workspace_bytes(2, 4, 60), dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.library().fa_bwd_varlen(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["cq"],
+        a["ck"], a["B"], a["H"], a["tq"], a["tk"], a["maxq"], a["maxk"], a["d"], a["scale"],
+        a["causal"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(lse=None), fa.FA_ERR_NULL), (dict(do=None), fa.FA_ERR_NULL),
+    (dict(dk=None), fa.FA_ERR_NULL), (dict(cq=None), fa.FA_ERR_NULL), (dict(ck=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(tq=0), fa.FA_ERR_SHAPE), (dict(tk=0), fa.FA_ERR_SHAPE),
+    (dict(maxq=0), fa.FA_ERR_SHAPE), (dict(maxk=0), fa.FA_ERR_SHAPE),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=1 << 16), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_VALUE), (dict(causal=3), fa.FA_ERR_VALUE),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=fa.bwd_workspace_bytes(2, 4, 60) - 1),
+                                           fa.FA_ERR_WORKSPACE),
+    (dict(maxq=129), fa.FA_ERR_WORKSPACE),  # 256 padded rows per pair against 128
+    (dict(q=P + 8), fa.FA_ERR_ALIGN), (dict(dv=P + 8), fa.FA_ERR_ALIGN), (dict(lse=P + 2), fa.FA_ERR_ALIGN),
+    (dict(ck=P + 2), fa.FA_ERR_ALIGN), (dict(ws=P + 4), fa.FA_ERR_ALIGN),
+])
+def test_bwd_varlen_rejects(kw, status):
+    assert _bwd_varlen(**kw) == status
+
+
 def _fp8(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=100, Nk=90, d=128, scale=0.1, qd=0.01, kd=0.02,
              vd=0.03, causal=1, stream=None)
