@@ -428,6 +428,46 @@ def bwd_bias_record(num: int, steps: int, warmup: int):
     return rec
 
 
+def bwd_varlen_record(steps: int, warmup: int):
+    """fa_bwd_varlen on the packed batch of the variable-length prefill leg with a seeded dO;
+    o and lse from fa_fwd_varlen (not timed)."""
+    import torch
+    import exact_tiled_attention_08_amd as fa
+    import workloads as W
+    q, k, v, cu, lens = W.make_varlen("cuda")
+    do = W.make_varlen_grad("cuda")
+    total, H, d = q.shape
+    scale = 1.0 / d ** 0.5
+    o, lse = fa.fwd_varlen(q, k, v, cu, cu, max(lens), scale=scale, causal=True)
+    dq = torch.empty((total, H, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    ws = torch.empty((fa.bwd_workspace_bytes(len(lens), H, max(lens)),), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        fa.bwd_varlen(q, k, v, o, lse, do, cu, cu, max(lens), max(lens), scale=scale, causal=True,
+                      dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    wall_ms, ev_ms = time_launches(step, steps, warmup)
+    flops = 2.5 * W.varlen_flops(lens)  # five contractions against the forward's two
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    rec = {
+        "workload": f"bf16 causal packed batch of {len(lens)} sequences, lengths uniform in "
+                    f"[256, 8192] (seed 60), {total} tokens, H={H} d={d}",
+        "flops_per_call": flops,
+        "flops_note": "the five contractions of the backward, 10*H*n*n*d per sequence, halved "
+                      "for the causal mask",
+        "ms_per_step": wall_ms, "kernel_ms": ev_ms,
+        "note": "kernel_ms spans the three launches of one call (statistics, dK/dV, dQ)",
+        "tflops": flops / (wall_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def decode_record(steps: int, warmup: int, cpu: bool = False):
     """fa_decode_splitkv on the decode workload; with cpu, also the oracle over every
     (b, h) of the same cache on the host's cores (cpu_baseline, full)."""
@@ -521,7 +561,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "paged", "varlen", "fp8",
-                                       "bias", "backward_bias"],
+                                       "bias", "backward_bias", "backward_varlen"],
                     default=None,
                     help="run one leg only (used under the profiler); 'copy' times a plain "
                          "1 GiB device copy, the reference for scaling HBM byte counters")
@@ -557,6 +597,9 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps({"backward": bwd_record(args.workload, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "backward_varlen":
+        print(json.dumps({"backward_varlen": bwd_varlen_record(args.steps, args.warmup)}), flush=True)
         return
     if args.only == "backward_bias":
         print(json.dumps({"backward_bias": bwd_bias_record(args.workload, args.steps, args.warmup)}),
@@ -638,6 +681,7 @@ def main():
         extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
         extra["backward_bias"] = bwd_bias_record(args.workload, max(5, args.steps // 2),
                                                  max(2, args.warmup // 2))
+        extra["backward_varlen"] = bwd_varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
         out["also"] = extra
     print(json.dumps(out), flush=True)
 

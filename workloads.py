@@ -162,6 +162,12 @@ def make_varlen(device="cpu", seed: int = 60):
     return q, k, v, cu, lens
 
 
+def make_varlen_grad(device="cpu", seed: int = 60):
+    """dO of the packed variable-length batch: bfloat16 N(0,1) [total, H, d], seed seed+4."""
+    total = sum(varlen_lengths(seed))
+    return draw((1, total, VARLEN_H, VARLEN_D), seed + 4, 1.0, torch.bfloat16, device)[0]
+
+
 def varlen_flops(lens, H: int = VARLEN_H, d: int = VARLEN_D, causal: bool = True) -> float:
     """Algorithmic FLOPs of the packed prefill: 4*H*n*n*d per sequence, halved if causal."""
     f = sum(4.0 * H * n * n * d for n in lens)
