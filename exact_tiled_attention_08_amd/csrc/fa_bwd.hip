@@ -28,6 +28,10 @@
 //      dK/dV workgroups with atomics: every output element is written once, in a fixed
 //      order, so the result is deterministic.
 //
+// The same three kernels serve packed batches of variable-length sequences (VARLEN): a
+// pair's rows are then one sequence of one head in [total][H][d] tensors (pair_view), and
+// workgroups whose tile lies past their sequence's end return before any barrier.
+//
 // MFMA layouts (v_mfma_f32_32x32x16_bf16, lane l, g = l / 32):
 //   A (32 x 16): row l%32, k = 8g..8g+7      B (16 x 32): col l%32, same k
 //   C (32 x 32): col l%32, row 8*(i/4) + 4g + i%4 for element i = 0..15
