@@ -51,9 +51,10 @@ def traffic_for(kind: str, workload: int):
     return ent.get("bytes_per_launch")
 
 
-def bwd_traffic(workload: int):
-    """HBM bytes of one fa_bwd call: the sum over its three kernels, or None unless all three
-    were measured on the current source."""
+def bwd_traffic(workload):
+    """HBM bytes of one backward call: the sum over its three kernels, or None unless all
+    three were measured on the current source. `workload`: 3 for fa_bwd on workload 3's
+    shape, "bias3" for fa_bwd_bias there, "varlen" for fa_bwd_varlen on the packed batch."""
     parts = [traffic_for(k, workload) for k in ("bwd_pre", "bwd_dkdv", "bwd_dq")]
     return None if any(p is None for p in parts) else sum(parts)
 
@@ -421,7 +422,8 @@ def bwd_bias_record(num: int, steps: int, warmup: int):
         "note": "kernel_ms spans the three launches of one call (statistics, dK/dV, dQ)",
         "tflops": w.bwd_flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": bwd_traffic(f"bias{num}")},
     }
     del q, k, v, bias, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
@@ -461,7 +463,8 @@ def bwd_varlen_record(steps: int, warmup: int):
         "note": "kernel_ms spans the three launches of one call (statistics, dK/dV, dQ)",
         "tflops": flops / (wall_ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": bwd_traffic("varlen")},
     }
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
