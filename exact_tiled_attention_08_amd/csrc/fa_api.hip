@@ -24,12 +24,15 @@ fa_status finish_launch(hipError_t e) {
 // (b, h) pairs handled together on one XCD (see fa::map_block). The XCD's CUs walk the
 // group's query tiles together, so each K/V tile is fetched into its L2 once per round of
 // concurrently running tiles of a head; with long sequences (many query tiles) fewer heads
-// per group mean more tiles of one head per round, hence fewer re-reads from HBM
-// (measured: 3% faster at 118 query tiles per head, no gain at 32).
+// per group mean more tiles of one head per round, hence fewer re-reads from HBM. Measured
+// on the forward with 118 query tiles per head (4 heads per XCD): HBM reads 7.3 / 3.8 /
+// 1.9 GB for 4 / 2 / 1 heads per group, 1132 / 1197 / 1208 TFLOP/s; with 32 query tiles
+// the order reverses (1066 / 1060 / 1039 TFLOP/s for 4 / 2 / 1 heads, though 1 head
+// halves the reads), so all of the XCD's heads form one group there.
 int heads_per_group(int BH, long long nqt) {
   if (BH % 8 != 0) return 1;
   const int per_xcd = BH / 8;
-  return (nqt > 64 && per_xcd % 2 == 0) ? 2 : per_xcd;
+  return nqt > 64 ? 1 : per_xcd;
 }
 
 // Key position of query row 0 under the causal mask: the queries are the last Nq positions

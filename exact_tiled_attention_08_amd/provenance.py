@@ -12,17 +12,21 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
+# Each kind's kernel source, the shared device header, and the host file that sets its
+# launch (grid, block -> tile mapping): a change to any of them can change what the counters
+# read.
+_COMMON = ["csrc/fa_internal.h", "csrc/fa_api.hip"]
 KERNEL_SOURCES = {
-    "fwd_bf16": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
-    "fwd_bf16_bias": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
-    "fwd_bf16_varlen": ["csrc/fa_fwd_bf16.hip", "csrc/fa_internal.h"],
-    "fwd_fp8": ["csrc/fa_fwd_fp8.hip", "csrc/fa_internal.h"],
-    "fwd_f32": ["csrc/fa_fwd_f32.hip", "csrc/fa_internal.h"],
-    "decode": ["csrc/fa_decode.hip", "csrc/fa_internal.h"],
-    "decode_paged": ["csrc/fa_decode.hip", "csrc/fa_internal.h"],
-    "bwd_pre": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
-    "bwd_dkdv": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
-    "bwd_dq": ["csrc/fa_bwd.hip", "csrc/fa_internal.h"],
+    "fwd_bf16": ["csrc/fa_fwd_bf16.hip", *_COMMON],
+    "fwd_bf16_bias": ["csrc/fa_fwd_bf16.hip", *_COMMON],
+    "fwd_bf16_varlen": ["csrc/fa_fwd_bf16.hip", *_COMMON],
+    "fwd_fp8": ["csrc/fa_fwd_fp8.hip", *_COMMON],
+    "fwd_f32": ["csrc/fa_fwd_f32.hip", *_COMMON],
+    "decode": ["csrc/fa_decode.hip", *_COMMON],
+    "decode_paged": ["csrc/fa_decode.hip", *_COMMON],
+    "bwd_pre": ["csrc/fa_bwd.hip", *_COMMON],
+    "bwd_dkdv": ["csrc/fa_bwd.hip", *_COMMON],
+    "bwd_dq": ["csrc/fa_bwd.hip", *_COMMON],
 }
 
 
