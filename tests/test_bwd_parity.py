@@ -216,8 +216,8 @@ def test_bwd_workload4_properties():
 def test_bwd_workload4_oracle():
     """N = 30000 causal at full size against the oracle: dQ on 64 sampled rows of every head;
     dK and dV on every key row of head (0, 0) (all 235 of its 128-key workgroups, in the
-    mapping that groups two heads per XCD run, which only heads of more than 64 key tiles
-    use) and on 64 sampled key rows of the last head."""
+    mapping that gives each head its own XCD group, which only heads of more than 64 key
+    tiles use) and on 64 sampled key rows of the last head."""
     w = W.WORKLOADS[4]
     say(f"bwd workload 4: {w.name} (oracle: sampled dQ rows, one full head of dK/dV)")
     q, k, v = W.make_inputs(w, DEV)
@@ -235,6 +235,37 @@ def test_bwd_workload4_oracle():
     got = {"dq": rows_of(dq, qrows, w.d), "dk": rows_of(dk, krows, w.d),
            "dv": rows_of(dv, krows, w.d)}
     st = compare_grads(got, {"dq": rq, "dk": rk, "dv": rv}, w.name)
+    say(f"  {st}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_long_heads_grid_mapping(causal):
+    """Heads of more than 64 key and query tiles of 128, two per XCD (B*H = 16): both main
+    kernels then give each head its own XCD group. Gradients start as NaN (every element
+    must be written); dQ on the first and last row of every 128-row query tile and dK, dV on
+    the first and last row of every 128-key tile of every head match the oracle."""
+    B, H, n, d = 2, 8, 8320, 64
+    say(f"bwd long heads B={B} H={H} N={n} d={d} causal={causal}")
+    q = seeded((B, H, n, d), 71, torch.bfloat16, mult=2.0)
+    k = seeded((B, H, n, d), 72, torch.bfloat16, mult=2.0)
+    v = seeded((B, H, n, d), 73, torch.bfloat16)
+    do = seeded((B, H, n, d), 74, torch.bfloat16)
+    scale = finite_scale(d)
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
+    g = [torch.full((B, H, n, d), float("nan"), device=DEV) for _ in range(3)]
+    fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, dq=g[0], dk=g[1], dv=g[2])
+    torch.cuda.synchronize()
+    assert not any(torch.isnan(t).any() for t in g)
+    rows = []
+    for bh in range(B * H):
+        for t0 in range(0, n, 128):
+            rows += [bh * n + t0, bh * n + min(n, t0 + 128) - 1]
+    say(f"  oracle: {len(rows)} rows of dQ and of dK/dV")
+    rq, rk, rv = oracle.attention_bwd(q.cpu(), k.cpu(), v.cpu(), do.cpu(), scale, causal,
+                                      qrows=rows, krows=rows)
+    got = {"dq": rows_of(g[0], rows, d), "dk": rows_of(g[1], rows, d), "dv": rows_of(g[2], rows, d)}
+    st = compare_grads(got, {"dq": rq, "dk": rk, "dv": rv}, "long heads")
     say(f"  {st}")
 
 

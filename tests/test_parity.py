@@ -130,6 +130,39 @@ def test_many_heads_grid_mapping(d):
                     torch.bfloat16, f"B={B} H={H}")
 
 
+def _tile_edge_rows(BH: int, n: int, tile: int):
+    """Flat rows (b*H + h)*n + i: the first and last row of every `tile`-row tile of every
+    (b, h), so that every (b, h, tile) of the grid is checked."""
+    rows = []
+    for bh in range(BH):
+        for t0 in range(0, n, tile):
+            rows += [bh * n + t0, bh * n + min(n, t0 + tile) - 1]
+    return rows
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_long_heads_grid_mapping(causal):
+    """Heads of more than 64 query tiles, two per XCD (B*H = 16): the block -> tile map then
+    gives each head its own XCD group. Outputs start as NaN (every element must be written)
+    and the first and last row of each of the 65 query tiles of every head match the
+    oracle."""
+    B, H, n, d = 2, 8, 16640, 64
+    say(f"long heads B={B} H={H} N={n} d={d} causal={causal}")
+    q = seeded((B, H, n, d), 41, torch.bfloat16, mult=2.0)
+    k = seeded((B, H, n, d), 42, torch.bfloat16, mult=2.0)
+    v = seeded((B, H, n, d), 43, torch.bfloat16)
+    o = torch.full((B, H, n, d), float("nan"), device=DEV)
+    lse = torch.full((B, H, n), float("nan"), device=DEV)
+    fa.fwd(q, k, v, scale=finite_scale(d), causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    rows = _tile_edge_rows(B * H, n, 256)
+    o_ref, l_ref = oracle_rows(q, k, v, finite_scale(d), causal, rows)
+    st = compare(rows_of(o, rows, d), rows_of(lse, rows), o_ref, l_ref, torch.bfloat16,
+                 "long heads")
+    say(f"  {st}")
+
+
 # ------------------------------------------------------------------ closed forms on the GPU
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
