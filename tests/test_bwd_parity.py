@@ -42,9 +42,15 @@ def _gpu():
 
 
 def _fwd_bwd(q, k, v, do, scale, causal):
+    """Forward, then backward into NaN-filled gradients, every element of which must be
+    written (zero where a row or key takes part in nothing)."""
     o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal)
+    dq = torch.full(q.shape, float("nan"), device=q.device)
+    dk = torch.full(k.shape, float("nan"), device=q.device)
+    dv = torch.full(v.shape, float("nan"), device=q.device)
+    fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
+    assert not any(torch.isnan(t).any() for t in (dq, dk, dv)), "gradient elements left unwritten"
     return dq, dk, dv
 
 

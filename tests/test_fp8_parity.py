@@ -94,8 +94,11 @@ def test_fp8_workload_sampled(num, per_head):
     w = W.WORKLOADS[num]
     say(f"fp8 workload {num}: {w.name}")
     (q8, qd), (k8, kd), (v8, vd) = W.make_inputs_fp8(w, DEV)
-    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal)
+    o = torch.full((w.B, w.H, w.Nq, w.d), float("nan"), device=DEV)
+    lse = torch.full((w.B, w.H, w.Nq), float("nan"), device=DEV)
+    fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
     torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()  # every element written
     rows = W.sample_rows(w, per_head)
     vdeq = _deq(v8, vd)
     o_ref, l_ref = oracle.attention(_deq(q8, qd), _deq(k8, kd), vdeq, w.scale, w.causal, rows=rows)

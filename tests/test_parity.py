@@ -53,7 +53,12 @@ def test_workload_sampled(num, per_head):
     w = W.WORKLOADS[num]
     say(f"workload {num}: {w.name} (sampled rows, {per_head} per head)")
     q, k, v = W.make_inputs(w, DEV)
-    o, lse = _run_fwd(q, k, v, w.scale, w.causal)
+    # outputs start as NaN: every element of the full-size output must be written
+    o = torch.full((w.B, w.H, w.Nq, w.d), float("nan"), device=DEV)
+    lse = torch.full((w.B, w.H, w.Nq), float("nan"), device=DEV)
+    fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
     rows = W.sample_rows(w, per_head)
     o_ref, l_ref = oracle_rows(q, k, v, w.scale, w.causal, rows)
     st = compare(rows_of(o, rows, w.d), rows_of(lse, rows), o_ref, l_ref, w.dtype, w.name)
@@ -66,8 +71,11 @@ def test_workload_decode_full_size():
     w = W.WORKLOADS[5]
     say(f"workload 5: {w.name}")
     q, k, v = W.make_inputs(w, DEV)
-    o, lse = fa.decode(q, k, v, num_splits=w.num_splits, scale=w.scale)
+    o = torch.full((w.B, w.H, 1, w.d), float("nan"), device=DEV)
+    lse = torch.full((w.B, w.H, 1), float("nan"), device=DEV)
+    fa.decode(q, k, v, num_splits=w.num_splits, scale=w.scale, out=o, lse=lse)
     torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()  # every (b, h) written
     BH = w.B * w.H
     pick = torch.tensor(sorted({0, 1, 31, 32, 255, 256, BH - 2, BH - 1, *range(7, BH, 37)}))
     qs = q.reshape(BH, 1, 1, w.d)[pick.to(DEV)].reshape(1, -1, 1, w.d)
