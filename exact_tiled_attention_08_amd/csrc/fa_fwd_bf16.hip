@@ -264,6 +264,16 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   const uint16_t* const lbase = loader ? kh : vh;
   const uint32_t lchunk = (loader ? koff : voff) - (uint32_t)(lrow * C::ROWB);
   const int wg4 = w & 3;  // wave index within its group
+  // Where group 1 issues its V tiles. Issuing one tile's direct loads holds the issuing
+  // waves for ~300-500 cycles (the CU accepts them at ~50-90 B/clk), so the issue belongs
+  // where a group has time to spare. At d = 128 (no bias) group 1 loads V_{j+1} at the start
+  // of its matrix phase of step j, into the buffer of V_{j-1}, which both groups finished
+  // reading at the barrier before; the vector phase it used to end, and which the other
+  // group's matrix phase waited for, then carries no load. Measured in one process: +1.2 to
+  // +1.5% at N = 8192 and +0.5 to +1.1% at N = 30000, bitwise-identical results; at d = 64
+  // it measured -0.9%, so there (and in the bias kernel, whose loads interleave with its
+  // bias tiles) group 1 keeps loading V_{j+2} at the end of its vector phase.
+  constexpr bool kVEarly = !BIAS && D == 128;
   auto dma = [&](int t, char* dst, int n) {
     const int kv0 = t * BC;
     if constexpr (kPoison) poison16(dst + (n * C::TL + 64 * wg4 + lane) * 16);
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qb[kk]));
   if (ntiles > 0) {
     wg_barrier();
-    if (ntiles > 1) issue(1, loader ? kbuf(1) : vbuf(1));
+    if (ntiles > 1 && (loader || !kVEarly)) issue(1, loader ? kbuf(1) : vbuf(1));
     if constexpr (BIAS)
       if (ntiles > 1) bias_issue(1);
     if (wave_kv_end > 0) {
@@ -495,13 +505,14 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // Step j < ntiles - 1: matrix phase (O += P_j V_j, then S for tile j+1 from K_{j+1}), a
   // barrier, then the vector phase (mask and softmax of tile j+1, rescale of O). Barriers
   // alternate between the groups' phases, so one group's matrix phase overlaps the other's
-  // vector phase. Both groups issue their next loads in the same interval between two
-  // barriers: group 0 loads K_{j+2} at the start of its matrix phase of step j, group 1
-  // loads V_{j+2} at the end of its vector phase of step j, which runs alongside group 0's
-  // matrix phase of step j+1. Each goes into the buffer of tile j, which both groups
-  // finished reading before that interval, and each group waits for its loads at the last
-  // barrier before the first reader: group 0 before its step j+1 matrix phase, group 1
-  // before its mid-step barrier of step j+1.
+  // vector phase. Group 0 loads K_{j+2} at the start of its matrix phase of step j, into
+  // the buffer of K_j, which both groups finished reading in their matrix phases of step
+  // j-1. Group 1 loads V_{j+2} at the end of its vector phase of step j, into the buffer of
+  // V_j (read by both groups' matrix phases of step j), or, with kVEarly, V_{j+1} at the
+  // start of its matrix phase of step j, into the buffer of V_{j-1}. Each group waits for
+  // its loads at the last barrier before their first reader: group 0 before its step j+1
+  // matrix phase, group 1 before its mid-step barrier of step j+1 (of step j with
+  // kVEarly: its V_{j+1} loads then have one matrix phase to land).
   //
   // With a bias, every wave also loads bias tile j+2 at the start of its vector phase of
   // step j, and reads bias tile j+1 (loaded one step earlier) in that phase. Group 0's
@@ -518,6 +529,8 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     }
     wg_barrier();
     if (loader && j + 2 < ntiles) issue(j + 2, kbuf(cur));
+    if constexpr (kVEarly)
+      if (!loader && j + 1 < ntiles) issue(j + 1, vbuf(cur ^ 1));  // V_{j+1}
     const bool active = j * BC < wave_kv_end;
     if (active) matrix.template operator()<true>(vbuf(cur), kbuf(cur ^ 1), pb, s);
     if (!loader) wait_loads();  // V_{j+1} (and the bias of tile j+1)
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
       if (needs_mask(j + 1)) mask_s(j + 1, s);
       softmax(s, pb);
     }
-    if (!loader && j + 2 < ntiles) issue(j + 2, vbuf(cur));
+    if (!kVEarly && !loader && j + 2 < ntiles) issue(j + 2, vbuf(cur));  // V_{j+2}
   };
   // Step ntiles - 1: PV of the last tile only (there is no next tile to score). The
   // barriers keep the same count as a full step, so both groups end the loop together.
