@@ -263,8 +263,14 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
       for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma8(kfrag(Ks, kb, kk), qb[kk], kk == 0 ? f32x16{} : s[kb]);
   };
 
-  // Prologue and steps: as in fa_fwd_bf16.hip (group 1 runs one phase behind group 0; each
-  // group issues its next tile loads two phases ahead of their first use).
+  // Prologue and steps: as in fa_fwd_bf16.hip (group 1 runs one phase behind group 0).
+  // Group 0 loads K_{j+2} at the start of its matrix phase of step j, into the buffer of K_j;
+  // group 1 loads V_{j+1} at the start of its matrix phase of step j, into the buffer of
+  // V_{j-1} (both groups finished reading it at the barrier before), and waits for it before
+  // its mid-step barrier. Issuing a tile's direct loads holds the issuing waves for a few
+  // hundred cycles, and here the vector phase is the longer one, so no load is issued in it
+  // (measured against group 1 loading V_{j+2} at the end of its vector phase: +6.7% at
+  // N = 8192 and +5.2% at N = 30000, bitwise-identical results).
   v8i pb[NKC];
   f32x16 s[NKB];
   if (ntiles > 0) issue(0, loader ? kbuf(0) : vbuf(0));
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qb[kk]));
   if (ntiles > 0) {
     wg_barrier();
-    if (ntiles > 1) issue(1, loader ? kbuf(1) : vbuf(1));
+    if (ntiles > 1 && loader) issue(1, kbuf(1));
     if (wave_kv_end > 0) {
       compute_s(kbuf(0), s);
       if (needs_mask(0)) mask_s(0, s);
@@ -288,6 +294,7 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
     if (loader) wait_loads();
     wg_barrier();
     if (loader && j + 2 < ntiles) issue(j + 2, kbuf(cur));
+    if (!loader && j + 1 < ntiles) issue(j + 1, vbuf(cur ^ 1));  // V_{j+1}
     const bool active = j * BC < wave_kv_end;
     if (active) matrix.template operator()<true>(vbuf(cur), kbuf(cur ^ 1), pb, s);
     if (!loader) wait_loads();
@@ -296,7 +303,6 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
       if (needs_mask(j + 1)) mask_s(j + 1, s);
       softmax(s, pb);
     }
-    if (!loader && j + 2 < ntiles) issue(j + 2, vbuf(cur));
   };
   auto last_step = [&](int j, int cur) {
     wg_barrier();
