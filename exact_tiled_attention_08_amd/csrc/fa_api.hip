@@ -3,6 +3,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
@@ -33,6 +36,77 @@ int heads_per_group(int BH, long long nqt) {
   if (BH % 8 != 0) return 1;
   const int per_xcd = BH / 8;
   return nqt > 64 ? 1 : per_xcd;
+}
+
+// Dynamic tail of a causal block map (fa::map_block_tail) over BH * nt tiles, hpg pairs
+// per XCD group, tiles in descending (desc) or ascending index order within a group;
+// weight(tile) is the tile's work in key or query tiles. Every XCD's run issues its tiles
+// heaviest first; its trailing items whose weight (plus two for the fixed part of a
+// workgroup) adds up to about kTailShare of the run's weight go to the shared pool, and
+// the grid gets kTailDraws ticket-drawing blocks per pool item, so an XCD that finishes
+// early can take up to that many times its share. Left off (draws = 0) when the runs are
+// not alike (BH not a multiple of 8) or hold fewer than two items per CU (32 CUs per XCD).
+// Measured on the bfloat16 prefill against the fixed map (bitwise-identical results):
+// +1.6% at N = 8192 and +2.3% at N = 30000 on one box, +0% and +2.9% on another (the gain
+// follows how unequal the box's XCDs run); per-CU busy time rose from 94-95% to 98%.
+// Non-causal launches (equal tiles, two per CU on the d = 64 shape) measured -1%, so they
+// keep the fixed map.
+constexpr double kTailShare = 0.08;
+constexpr double kTailDraws = 2.0;
+std::atomic<unsigned> g_tail_seq{0};
+
+template <typename Weight>
+fa::TailMap tail_map(int BH, int nt, int hpg, bool desc, Weight weight) {
+  fa::TailMap tm{};
+  if (BH % 8 != 0) return tm;
+  const long long per = (long long)BH * nt / 8;
+  if (per < 64) return tm;
+  // weight of run position t (run 0; all runs follow the same tile order)
+  auto at = [&](long long t) {
+    const long long j = t % ((long long)hpg * nt);
+    const int i = (int)(j / hpg);
+    return weight(desc ? nt - 1 - i : i) + 2;
+  };
+  double total = 0;
+  for (long long t = 0; t < per; ++t) total += (double)at(t);
+  long long pool = 0;
+  double acc = 0;
+  while (pool < per && acc < kTailShare * total) acc += (double)at(per - 1 - pool++);
+  if (pool == 0 || pool == per) return tm;
+  if (8 * per + 8 * (long long)(pool * kTailDraws) > INT32_MAX) return tm;  // grid size
+  tm.per = (int)per;
+  tm.s = (int)(per - pool);
+  tm.pool = (int)pool;
+  tm.draws = (int)(8 * pool * kTailDraws);
+  return tm;
+}
+
+int tail_slot() { return (int)(g_tail_seq.fetch_add(1, std::memory_order_relaxed) % fa::kTailSlots); }
+
+// Causal prefill: key tiles of bc keys that query tile qt (br rows) sees.
+fa::TailMap prefill_tail(const fa::FwdParams& p, int br, int bc) {
+  return tail_map(p.BH, p.nqt, p.hpg, true, [&](int qt) {
+    const long long last_q = std::min((long long)(qt + 1) * br, (long long)p.Nq) - 1;
+    const long long kv_end = std::min((long long)p.Nk, last_q + p.off + 1);
+    return kv_end > 0 ? (kv_end + bc - 1) / bc : 0;
+  });
+}
+
+// Causal backward: dK/dV tile kt is seen by the queries from max(0, kt*rows - off) on
+// (in tiles of rows queries); dQ tile qt sees the keys up to its last row + off.
+void backward_tails(fa::BwdParams& p) {
+  const int rk = fa::kBwdKeyRows, rq = fa::kBwdQueryRows;
+  p.tail_kv = tail_map(p.BH, p.nkt, p.hpg_kv, false, [&](int kt) {
+    const long long q_first = std::max(0LL, (long long)kt * rk - p.off);
+    return q_first < p.Nq ? (p.Nq - q_first + rq - 1) / rq : 0;
+  });
+  p.tail_q = tail_map(p.BH, p.nqt, p.hpg_q, true, [&](int qt) {
+    const long long last_q = std::min((long long)(qt + 1) * rq, (long long)p.Nq) - 1;
+    const long long kv_end = std::min((long long)p.Nk, last_q + p.off + 1);
+    return kv_end > 0 ? (kv_end + rk - 1) / rk : 0;
+  });
+  p.slot_kv = tail_slot();
+  p.slot_q = tail_slot();
 }
 
 // Key position of query row 0 under the causal mask: the queries are the last Nq positions
@@ -91,6 +165,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, float* o, float* l
   p.nqt = (int)nqt;
   p.hpg = heads_per_group((int)BH, nqt);
   p.c = scale * fa::kLog2e;
+  if (dtype == FA_BF16 && causal != 0) {
+    p.tail = prefill_tail(p, br, fa::fwd_bf16_key_tile(d));
+    p.tail_slot = tail_slot();
+  }
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(p, d, causal != 0, (hipStream_t)stream)
                                   : fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream);
@@ -231,6 +309,10 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float* o, floa
   p.nqt = (int)nqt;
   p.hpg = heads_per_group((int)BH, nqt);
   p.c = c;
+  if (causal != 0) {
+    p.tail = prefill_tail(p, br, fa::fwd_fp8_key_tile());
+    p.tail_slot = tail_slot();
+  }
   p.vscale = v_descale;
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   return finish_launch(fa::launch_fwd_fp8(p, causal != 0, (hipStream_t)stream));
@@ -398,6 +480,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
   p.hpg_q = heads_per_group((int)BH, nqt);
   p.scale = scale;
   p.c = scale * fa::kLog2e;
+  if (dtype == FA_BF16 && causal != 0) backward_tails(p);
   (void)hipGetLastError();  // drop a stale error left by unrelated work on this thread
   if (dtype == FA_F32) return finish_launch(fa::launch_bwd_f32(p, d, causal != 0, (hipStream_t)stream));
   return finish_launch(fa::launch_bwd(p, d, causal != 0, (hipStream_t)stream));

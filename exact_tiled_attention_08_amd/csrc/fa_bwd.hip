@@ -52,6 +52,10 @@
 namespace fa {
 namespace {
 
+// Ticket counters of the dynamic tails (map_block_tail) of the dK/dV and dQ kernels, zero
+// at load and put back to zero by the last ticket of every launch.
+__device__ unsigned g_tail_tickets[kTailSlots];
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -216,7 +220,14 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // Low key tiles see the most queries under the causal mask; ascending order issues them first.
   int bh, kt;
-  map_block(blockIdx.x, gridDim.x, p.nkt, p.hpg_kv, false, bh, kt);
+  // (not compiled into the biased instances: it costs them registers)
+  if (VARLEN || BIAS || p.tail_kv.draws == 0) {
+    map_block(blockIdx.x, gridDim.x, p.nkt, p.hpg_kv, false, bh, kt);
+  } else {
+    __shared__ int s_item;
+    if (!map_block_tail(p.tail_kv, &g_tail_tickets[p.slot_kv], &s_item, p.nkt, p.hpg_kv, false, bh, kt))
+      return;  // the pool was empty: no item for this workgroup
+  }
   const int k0 = kt * kBwdKeyRows;
   const int kw0 = k0 + 32 * w;  // first key of this wave
   const int key = kw0 + col;    // this lane's key
@@ -527,7 +538,14 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
   const int col = lane & 31;
 
   int bh, qt;
-  map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg_q, CAUSAL, bh, qt);
+  // (not compiled into the biased instances: it costs them registers)
+  if (VARLEN || BIAS || p.tail_q.draws == 0) {
+    map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg_q, CAUSAL, bh, qt);
+  } else {
+    __shared__ int s_item;
+    if (!map_block_tail(p.tail_q, &g_tail_tickets[p.slot_q], &s_item, p.nqt, p.hpg_q, CAUSAL, bh, qt))
+      return;  // the pool was empty: no item for this workgroup
+  }
   const int q0 = qt * kBwdQueryRows;
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + col;
@@ -721,7 +739,8 @@ hipError_t launch(const BwdParams& prm, bool causal, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned nkv = (unsigned)(p.BH * p.nkt), nq = (unsigned)(p.BH * p.nqt);
+  const unsigned nkv = (unsigned)(p.tail_kv.draws ? 8 * p.tail_kv.s + p.tail_kv.draws : p.BH * p.nkt);
+  const unsigned nq = (unsigned)(p.tail_q.draws ? 8 * p.tail_q.s + p.tail_q.draws : p.BH * p.nqt);
   if constexpr (BIAS) {
     if (causal) {
       if (p.dbias)

@@ -65,6 +65,10 @@
 namespace fa {
 namespace {
 
+// Ticket counters of the dynamic tail (map_block_tail), zero at load and put back to zero
+// by the last ticket of every launch.
+__device__ unsigned g_tail_tickets[kTailSlots];
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -176,7 +180,15 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   const int col = lane & 31;
 
   int bh, qt;
-  map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg, CAUSAL, bh, qt);
+  // (the biased kernel, bound by HBM, measured no gain from the dynamic tail and keeps the
+  // fixed map)
+  if (VARLEN || BIAS || p.tail.draws == 0) {
+    map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg, CAUSAL, bh, qt);
+  } else {
+    __shared__ int s_item;
+    if (!map_block_tail(p.tail, &g_tail_tickets[p.tail_slot], &s_item, p.nqt, p.hpg, CAUSAL, bh, qt))
+      return;  // the pool was empty: no item for this workgroup
+  }
   const int q0 = qt * C::BR;
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + col;   // this lane's query row
@@ -597,7 +609,7 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
 template <int D, int BC, bool VARLEN, bool BIAS = false>
 hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
   FwdParams p = prm;
-  const int total = p.BH * p.nqt;
+  const int total = p.tail.draws ? 8 * p.tail.s + p.tail.draws : p.BH * p.nqt;
   if (causal)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true, VARLEN, BIAS>), dim3(total), dim3(64 * kNW), 0, s, p);
   else
@@ -608,6 +620,8 @@ hipError_t launch(const FwdParams& prm, bool causal, hipStream_t s) {
 }  // namespace
 
 int fwd_bf16_block_rows(int) { return 32 * kNW; }
+
+int fwd_bf16_key_tile(int d) { return d == 128 ? 96 : 128; }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s) {
   if (d == 128) return launch<128, 96, false>(p, causal, s);

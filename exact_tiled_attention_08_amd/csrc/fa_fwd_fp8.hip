@@ -48,6 +48,10 @@ constexpr int ROWB = D;              // bytes per K or V row
 constexpr int CHR = D / 16;          // 16-byte chunks per row (8)
 constexpr int TILEB = BC * ROWB;     // 16 KB
 constexpr int LDS = 4 * TILEB;       // two K buffers, two V buffers
+
+// Ticket counters of the dynamic tail (map_block_tail), zero at load and put back to zero
+// by the last ticket of every launch.
+__device__ unsigned g_tail_tickets[kTailSlots];
 constexpr int LOADS = BC * CHR / TL; // direct loads per thread per tile (4)
 constexpr int ROWSTEP = TL / CHR;    // 32
 constexpr int NKB = BC / 32;         // 32-key blocks per tile (4)
@@ -90,7 +94,13 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
   const int col = lane & 31;
 
   int bh, qt;
-  map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg, CAUSAL, bh, qt);
+  if (p.tail.draws == 0) {
+    map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg, CAUSAL, bh, qt);
+  } else {
+    __shared__ int s_item;
+    if (!map_block_tail(p.tail, &g_tail_tickets[p.tail_slot], &s_item, p.nqt, p.hpg, CAUSAL, bh, qt))
+      return;  // the pool was empty: no item for this workgroup
+  }
   const int Nq = p.Nq, Nk = p.Nk, off = p.off;
   const int q0 = qt * BR;
   const int wq0 = q0 + 32 * w;
@@ -347,9 +357,11 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
 
 int fwd_fp8_block_rows() { return BR; }
 
+int fwd_fp8_key_tile() { return BC; }
+
 hipError_t launch_fwd_fp8(const FwdParams& prm, bool causal, hipStream_t s) {
   FwdParams p = prm;
-  const int total = p.BH * p.nqt;
+  const int total = p.tail.draws ? 8 * p.tail.s + p.tail.draws : p.BH * p.nqt;
   if (causal)
     hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3(total), dim3(T), 0, s, p);
   else

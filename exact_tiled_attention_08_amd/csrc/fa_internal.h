@@ -15,6 +15,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplits = 1024;  // largest num_splits of the split-KV decode
 
+// Ticket-counter slots of the dynamic tail: a call takes the next slot of a ring, so calls
+// that overlap on one GPU (different streams) use different counters.
+constexpr int kTailSlots = 4096;
+// Dynamic tail of the block map (map_block_tail); draws == 0: the fixed map_block.
+struct TailMap {
+  int per;    // items per run (the grid covers 8 * per items)
+  int s;      // fixed items per run
+  int pool;   // pool items per run (per - s)
+  int draws;  // blocks that draw a ticket: gridDim.x - 8 * s
+};
+
 // Arguments of the prefill kernels (one struct keeps the launch signature small).
 struct FwdParams {
   const void* q;
@@ -46,6 +57,10 @@ struct FwdParams {
   long long bsb;
   long long bsh;
   long long bsq;
+  // Causal bfloat16 and FP8 prefill: the dynamic tail of the block map and its
+  // ticket-counter slot.
+  TailMap tail;
+  int tail_slot;
 };
 
 struct DecodeParams {
@@ -118,6 +133,12 @@ struct BwdParams {
   int total_q;
   int total_k;
   int top_left;
+  // Causal bfloat16 backward (dense, no bias): the dynamic tails of the dK/dV and dQ block
+  // maps and their ticket-counter slots.
+  TailMap tail_kv;
+  TailMap tail_q;
+  int slot_kv;
+  int slot_q;
 };
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence would also wait
@@ -178,6 +199,7 @@ hipError_t launch_fwd_bf16_bias(const FwdParams& p, int d, bool causal, hipStrea
 hipError_t launch_fwd_f32_bias(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, hipStream_t s);
 int fwd_fp8_block_rows();
+int fwd_fp8_key_tile();  // keys per K/V tile of the FP8 kernel
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, bool bf16, hipStream_t s);
@@ -191,6 +213,7 @@ hipError_t launch_bwd_f32(const BwdParams& p, int d, bool causal, hipStream_t s)
 
 // Query rows per workgroup of each prefill kernel (host needs it for the grid).
 int fwd_bf16_block_rows(int d);
+int fwd_bf16_key_tile(int d);  // keys per K/V tile of fa_fwd's bfloat16 kernel
 int fwd_f32_block_rows(int d);
 
 // Key rows per dK/dV workgroup and query rows per dQ workgroup of the backward pass.
@@ -205,16 +228,55 @@ constexpr int kBwdQueryRows = 128;
 // `hpg` heads query-tile by query-tile, so the query tiles of one head run
 // together on one XCD and share its K/V in L2. For causal attention the query
 // tiles are issued heaviest (most key tiles) first, which evens out the tail.
-__device__ __forceinline__ void map_block(int L, int total, int nqt, int hpg, bool causal,
-                                          int& bh, int& qt) {
-  const int per = total >> 3;
-  const int n = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
+// Item n of the renumbered order -> (b*H + h, query tile).
+__device__ __forceinline__ void map_item(int n, int nqt, int hpg, bool causal, int& bh, int& qt) {
   const int span = hpg * nqt;
   const int grp = n / span;
   const int j = n - grp * span;
   const int qi = j / hpg;
   qt = causal ? (nqt - 1 - qi) : qi;
   bh = grp * hpg + (j - qi * hpg);
+}
+
+__device__ __forceinline__ void map_block(int L, int total, int nqt, int hpg, bool causal,
+                                          int& bh, int& qt) {
+  const int per = total >> 3;
+  const int n = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
+  map_item(n, nqt, hpg, causal, bh, qt);
+}
+
+// The same map with a dynamic tail. The XCDs do not run at one speed: on the same tiles a
+// whole XCD can take ~10% longer than another (per-workgroup real-time stamps; which XCDs
+// are slow changes with the data's placement, not from run to run), and a fixed map ends
+// when the slowest XCD does. Here the first `s` items of each XCD's run stay fixed (block
+// L = 8t + x runs item t of run x, t < s); the remaining `pool` items of every run (the
+// lightest ones: runs issue heaviest first) form one pool, interleaved across the runs
+// so that it too is ordered heaviest first, and every later block takes the next pool
+// item with one atomic increment of a ticket counter. An XCD that finishes its fixed
+// items early therefore takes more of the pool. There are `draws` later blocks, more
+// than pool items, so an XCD can take more than its share; a block that draws a ticket
+// past the pool exits at once. Exactly `draws` tickets are drawn per launch, and the
+// block that draws the last one puts the counter back to 0 for the next launch that uses
+// it. `*s_item` is workgroup-shared scratch. Returns false when the block has no item.
+__device__ __forceinline__ bool map_block_tail(const TailMap& tm, unsigned* tickets, int* s_item,
+                                               int nqt, int hpg, bool causal, int& bh, int& qt) {
+  const int L = blockIdx.x;
+  const int t = L >> 3;
+  int n;
+  if (t < tm.s) {
+    n = (L & 7) * tm.per + t;
+  } else {
+    if (threadIdx.x == 0) {
+      const unsigned k = atomicAdd(tickets, 1u);
+      if (k + 1 == (unsigned)tm.draws) atomicExch(tickets, 0u);
+      *s_item = k < 8u * (unsigned)tm.pool ? (int)(k & 7) * tm.per + tm.s + (int)(k >> 3) : -1;
+    }
+    __syncthreads();
+    n = *s_item;
+    if (n < 0) return false;
+  }
+  map_item(n, nqt, hpg, causal, bh, qt);
+  return true;
 }
 
 }  // namespace fa

@@ -171,6 +171,87 @@ def test_long_heads_grid_mapping(causal):
     say(f"  {st}")
 
 
+# Causal bfloat16 launches whose B*H is a multiple of 8, with at least 64 query tiles per
+# XCD run, hand the lightest tiles of every run out through a ticket counter (one slot of a
+# ring of 4096 per call, put back to zero by the last ticket of the launch); the tests
+# below use such shapes.
+
+@pytest.mark.parametrize("d,causal,nq,nk", [(128, 1, 4096, 4000), (128, 2, 4000, 4096), (64, 1, 2048, 2048)],
+                         ids=["d128-bottom-right", "d128-top-left", "d64"])
+def test_dynamic_tail_oracle(d, causal, nq, nk):
+    """Outputs start as NaN (every element must be written) and the first and last row of
+    every query tile of every head match the oracle."""
+    B, H = (2, 16) if d == 128 else (4, 16)
+    say(f"dynamic tail B={B} H={H} Nq={nq} Nk={nk} d={d} causal={causal}")
+    q = seeded((B, H, nq, d), 51, torch.bfloat16, mult=2.0)
+    k = seeded((B, H, nk, d), 52, torch.bfloat16, mult=2.0)
+    v = seeded((B, H, nk, d), 53, torch.bfloat16)
+    o = torch.full((B, H, nq, d), float("nan"), device=DEV)
+    lse = torch.full((B, H, nq), float("nan"), device=DEV)
+    fa.fwd(q, k, v, scale=finite_scale(d), causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    rows = _tile_edge_rows(B * H, nq, 256)
+    o_ref, l_ref = oracle_rows(q, k, v, finite_scale(d), causal, rows)
+    st = compare(rows_of(o, rows, d), rows_of(lse, rows), o_ref, l_ref, torch.bfloat16,
+                 "dynamic tail")
+    say(f"  {st}")
+
+
+def _count_mismatches(o, lse, o_ref, l_ref, bad):
+    # NaN compares unequal, so an element left unwritten counts as a mismatch
+    bad += ((o != o_ref).any() | (lse != l_ref).any()).to(torch.int32)
+
+
+def test_dynamic_tail_counter_reuse():
+    """4100 launches in a row, more than the 4096 counter slots, so every slot is used again
+    after the launch before put it back to zero: each launch writes every element of its
+    NaN-filled outputs and matches the first launch bitwise."""
+    B, H, n, d = 64, 8, 256, 128  # 512 one-tile heads: 64 items per XCD run
+    say(f"dynamic tail counter reuse B={B} H={H} N={n} d={d}, 4100 launches")
+    q = seeded((B, H, n, d), 61, torch.bfloat16, mult=2.0)
+    k = seeded((B, H, n, d), 62, torch.bfloat16, mult=2.0)
+    v = seeded((B, H, n, d), 63, torch.bfloat16)
+    o_ref, l_ref = fa.fwd(q, k, v, scale=finite_scale(d), causal=True)
+    o = torch.empty_like(o_ref)
+    lse = torch.empty_like(l_ref)
+    bad = torch.zeros((), dtype=torch.int32, device=DEV)
+    for _ in range(4100):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        fa.fwd(q, k, v, scale=finite_scale(d), causal=True, out=o, lse=lse)
+        _count_mismatches(o, lse, o_ref, l_ref, bad)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o_ref).any()
+    assert int(bad) == 0, f"{int(bad)} of 4100 launches differ from the first"
+
+
+def test_dynamic_tail_two_streams():
+    """Calls on two streams at once take different counter slots: interleaved launches on
+    two streams, each into its own NaN-filled outputs, all match a lone launch bitwise."""
+    B, H, n, d = 2, 16, 4096, 128
+    say(f"dynamic tail on two streams B={B} H={H} N={n} d={d}")
+    q = seeded((B, H, n, d), 71, torch.bfloat16, mult=2.0)
+    k = seeded((B, H, n, d), 72, torch.bfloat16, mult=2.0)
+    v = seeded((B, H, n, d), 73, torch.bfloat16)
+    o_ref, l_ref = fa.fwd(q, k, v, scale=finite_scale(d), causal=True)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs = [(torch.empty_like(o_ref), torch.empty_like(l_ref)) for _ in streams]
+    bads = [torch.zeros((), dtype=torch.int32, device=DEV) for _ in streams]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(20):
+        for s, (o, lse), bad in zip(streams, bufs, bads):
+            with torch.cuda.stream(s):
+                o.fill_(float("nan"))
+                lse.fill_(float("nan"))
+                fa.fwd(q, k, v, scale=finite_scale(d), causal=True, out=o, lse=lse)
+                _count_mismatches(o, lse, o_ref, l_ref, bad)
+    torch.cuda.synchronize()
+    assert [int(b) for b in bads] == [0, 0]
+
+
 # ------------------------------------------------------------------ closed forms on the GPU
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
