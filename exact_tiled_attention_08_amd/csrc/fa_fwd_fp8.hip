@@ -333,24 +333,52 @@ __global__ __launch_bounds__(T, 2) void fwd_fp8_kernel(FwdParams p) {
   }
 
   // Epilogue: O = v_descale * acc / l; LSE = ln2 * (m + log2 l - 8) (l holds 2^8-scaled sums).
+  // O leaves through this wave's own 8 KB of LDS, 64 columns at a time, so that each store
+  // writes whole 256-byte segments of 4 rows rather than 32 bytes of each of 32 rows (as in
+  // the bfloat16 kernel; chunk c of row r at chunk position c ^ (r % 16), free of bank
+  // conflicts). Every wave has passed its last LDS read at the barrier above.
   const float lt = wave_half_sum(l);
-  if (qrow < Nq) {
-    const float f = lt > 0.f ? p.vscale / lt : 0.f;
-    float* orow = p.o + ((size_t)bh * Nq + qrow) * D;
+  const float f = lt > 0.f ? p.vscale / lt : 0.f;
+  constexpr int kStage = 32 * 64 * 4;  // one wave's area
+  static_assert(NW * kStage <= LDS, "epilogue staging exceeds the LDS");
+  char* const ot = smem + w * kStage;
+  float* const oh = p.o + (size_t)bh * Nq * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int hh = 0; hh < D / 64; ++hh) {
+#pragma unroll
+    for (int dbh = 0; dbh < 2; ++dbh)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
+        const int db = 2 * hh + dbh;
         f32x4 val;
         val[0] = oacc[db][4 * jj + 0] * f;
         val[1] = oacc[db][4 * jj + 1] * f;
         val[2] = oacc[db][4 * jj + 2] * f;
         val[3] = oacc[db][4 * jj + 3] * f;
-        *(f32x4*)(orow + 32 * db + 8 * jj + 4 * g) = val;
+        const int c = 8 * dbh + 2 * jj + g;  // columns 64 hh + 4c .. 64 hh + 4c + 3
+        *(f32x4*)(ot + col * 256 + ((c ^ (col & 15)) << 4)) = val;
       }
-    if (g == 0 && p.lse)
-      p.lse[(size_t)bh * Nq + qrow] = lt > 0.f ? (m + __log2f(lt) - 8.f) * kLn2 : -INFINITY;
+    asm volatile("" ::: "memory");  // one wave's LDS accesses complete in issue order
+    const int c = lane & 15;
+    f32x4 rd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      rd[i] = *(const f32x4*)(ot + r * 256 + ((c ^ (r & 15)) << 4));
+    }
+    float* const obase = oh + (size_t)(wq0 + (lane >> 4)) * D + 64 * hh + 4 * c;
+    if (wq0 + 32 <= Nq) {  // all 32 rows of the wave exist
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(f32x4*)(obase + (size_t)(4 * i) * D) = rd[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (wq0 + 4 * i + (lane >> 4) < Nq) *(f32x4*)(obase + (size_t)(4 * i) * D) = rd[i];
+    }
+    asm volatile("" ::: "memory");
   }
+  if (qrow < Nq && g == 0 && p.lse)
+    p.lse[(size_t)bh * Nq + qrow] = lt > 0.f ? (m + __log2f(lt) - 8.f) * kLn2 : -INFINITY;
 }
 
 }  // namespace
