@@ -591,11 +591,13 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // hold 16-byte pieces of one row, so storing them directly writes 32 bytes of each of 32
   // rows per instruction; read back row-major, each store writes whole 256-byte segments
   // of 4 rows (same process, bitwise-identical results: +1.1-1.2% at N = 8192, +1.4% on the
-  // d = 64 shape). Every wave has passed its last LDS read (the barrier after the last PV
-  // product), so the K/V buffers are free. Chunk c of row r sits at chunk position
-  // c ^ (r % 16): both the writes and the reads are then free of bank conflicts. (Group 0
-  // staging in the K buffers and storing while group 1 ran its last PV product measured
-  // slower.)
+  // d = 64 shape). The stores are non-temporal: O is written once and never read here, and
+  // streaming it past L2 leaves the K/V tiles there (a further +1.2% at N = 8192 and +1.6%
+  // on the d = 64 shape; with the scattered 32-byte pattern the same hint had been slower).
+  // Every wave has passed its last LDS read (the barrier after the last PV product), so the
+  // K/V buffers are free. Chunk c of row r sits at chunk position c ^ (r % 16): both the
+  // writes and the reads are then free of bank conflicts. (Group 0 staging in the K buffers
+  // and storing while group 1 ran its last PV product measured slower.)
   const float lt = wave_half_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   constexpr int kStage = 32 * 64 * 4;  // one wave's area
@@ -627,11 +629,12 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     float* const obase = oh + (size_t)(wq0 + (lane >> 4)) * rs + 64 * hh + 4 * c;
     if (wq0 + 32 <= Nq) {  // all 32 rows of the wave exist
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *(f32x4*)(obase + (size_t)(4 * i) * rs) = rd[i];
+      for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(rd[i], (f32x4*)(obase + (size_t)(4 * i) * rs));
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (wq0 + 4 * i + (lane >> 4) < Nq) *(f32x4*)(obase + (size_t)(4 * i) * rs) = rd[i];
+        if (wq0 + 4 * i + (lane >> 4) < Nq)
+          __builtin_nontemporal_store(rd[i], (f32x4*)(obase + (size_t)(4 * i) * rs));
     }
     asm volatile("" ::: "memory");
   }
