@@ -170,7 +170,9 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   static_assert(!(BIAS && VARLEN), "bias is offered for dense batches only");
   using BCfg = BiasCfg<BIAS ? BC : 64>;
   constexpr int BIASLDS = BIAS ? BCfg::LDS : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS + BIASLDS];
+  // Q staging (no bias): each wave's 32 query rows, loaded global -> LDS in whole rows
+  constexpr int QSTAGE = BIAS ? 0 : kNW * 32 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS + BIASLDS + QSTAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,8 +187,10 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   if (VARLEN || BIAS || p.tail.draws == 0) {
     map_block(blockIdx.x, gridDim.x, p.nqt, p.hpg, CAUSAL, bh, qt);
   } else {
-    __shared__ int s_item;
-    if (!map_block_tail(p.tail, &g_tail_tickets[p.tail_slot], &s_item, p.nqt, p.hpg, CAUSAL, bh, qt))
+    // the draw's result passes through K buffer 1, which no load writes before the first
+    // barrier of the prologue (every wave has read it by then)
+    int* const s_item = (int*)(smem + C::TILEB);
+    if (!map_block_tail(p.tail, &g_tail_tickets[p.tail_slot], s_item, p.nqt, p.hpg, CAUSAL, bh, qt))
       return;  // the pool was empty: no item for this workgroup
   }
   const int q0 = qt * C::BR;
@@ -239,14 +243,42 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
     bw = (const uint16_t*)p.bias + (size_t)b * p.bsb + (size_t)h * p.bsh + (size_t)bias_r0 * p.bsq;
   }
 
-  // Q tile stays in VGPRs for the whole key loop, as the B operand of S^T = K Q^T.
+  // Q tile stays in VGPRs for the whole key loop, as the B operand of S^T = K Q^T. A lane
+  // needs 16-byte pieces of one row, so loading them directly reads 32 bytes of each of 32
+  // rows per instruction. Without a bias, the wave's rows instead go global -> LDS in whole
+  // rows (direct loads, chunk c of row r at chunk position c ^ (r % CHR), issued together
+  // with the first K/V tile) and are read into VGPRs once those loads have landed (same
+  // process, bitwise-identical results: +0.35-0.5% on the three bf16 prefill shapes; a
+  // timing-only copy that loaded the same bytes contiguously straight into the wrong lanes
+  // gained 1.5% at N = 8192, so the LDS round trip costs most of what the pattern saves).
+  // Rows past Nq load row Nq - 1: their scores stay finite, and they are never stored.
   bf16x8 qb[D / 16];
+  char* const qstage = smem + C::LDS + BIASLDS + w * (32 * D * 2);
+  if constexpr (BIAS) {
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (qrow < Nq)
-      qb[kk] = *(const bf16x8*)(qh + (size_t)qrow * rs + 16 * kk + 8 * g);
-    else
-      qb[kk] = bf16x8{};
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (qrow < Nq)
+        qb[kk] = *(const bf16x8*)(qh + (size_t)qrow * rs + 16 * kk + 8 * g);
+      else
+        qb[kk] = bf16x8{};
+    }
+  } else {
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    const uint32_t qlds = (uint32_t)(uintptr_t)((lds_char*)qstage);
+    const int qr0 = min(wq0, Nq - 1);        // base row (a wave past Nq re-reads row Nq - 1)
+    const int rlast = min(31, Nq - 1 - qr0);  // last row from the base that lies below Nq
+    const char* const qbase = (const char*)qh + (size_t)qr0 * rs * 2;
+    // an opaque copy of the lane index: the epilogue's store addresses have the same form,
+    // and the compiler would otherwise keep these terms alive across the key loop (spills)
+    int ql = lane;
+    asm volatile("" : "+v"(ql));
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const int slot = 64 * n + ql;
+      const int r = slot / CPR, pos = slot % CPR;
+      const int c = pos ^ (r % CPR);
+      dma16(qbase, (uint32_t)(min(r, rlast) * rs * 2 + 16 * c), qlds + 1024u * n);
+    }
   }
 
   // Key tiles this workgroup visits, and the key bound of this wave (causal).
@@ -494,6 +526,13 @@ __global__ __launch_bounds__(64 * kNW, 2) void fwd_bf16_kernel(FwdParams p) {
   // that the Q loads are complete, so it does not re-wait for them inside the loop (where
   // the wait would also stall on the in-flight tile loads that share the counter).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unchanged
+  if constexpr (!BIAS) {
+    asm volatile("" ::: "memory");  // the Q rows are in LDS now
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qb[kk] = *(const bf16x8*)(qstage + col * (D * 2) + (((2 * kk + g) ^ (col % CPR)) << 4));
+  }
   // The compiler merges control flow so that some path into the loop bypasses that wait;
   // it would then wait for the Q loads again before the first S^T MFMA of every matrix
   // phase, and that vmcnt(0) would also stall on the tile loads just issued. Passing Q
