@@ -496,24 +496,17 @@ __global__ __launch_bounds__(kT, 1) void bwd_dkdv_kernel(BwdParams p) {
     pin(dk, dv);
   }
 
-  // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4.
-  if (key < Nk) {
-    float* dkr = p.dk + pv.kbase + (size_t)key * rs;
-    float* dvr = p.dv + pv.kbase + (size_t)key * rs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 a, b;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a[u] = dk[db][4 * j + u] * p.scale;
-          b[u] = dv[db][4 * j + u];
-        }
-        *(f32x4*)(dkr + 32 * db + 8 * j + 4 * g) = a;
-        *(f32x4*)(dvr + 32 * db + 8 * j + 4 * g) = b;
-      }
-  }
+  // dK^T and dV^T: lane column = key, element i = dim 32db + 8(i/4) + 4g + i%4. They go out
+  // through LDS in whole row segments (store_rows_staged), once every wave has finished
+  // with the Q/dO stages.
+  wait_loads();
+  wg_barrier();
+  static_assert((kT / 64) * 32 * 64 * 4 <= (int)sizeof(smem), "epilogue staging exceeds the LDS");
+  char* const stg = smem + w * (32 * 64 * 4);
+  float* const kout = p.dk + pv.kbase + (size_t)kw0 * rs;
+  float* const vout = p.dv + pv.kbase + (size_t)kw0 * rs;
+  store_rows_staged<D>(dk, p.scale, stg, kout, (size_t)rs, Nk - kw0, lane);
+  store_rows_staged<D>(dv, 1.f, stg, vout, (size_t)rs, Nk - kw0, lane);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -716,19 +709,14 @@ __global__ __launch_bounds__(kT, 2) void bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  // dQ^T: lane column = query, element i = dim 32db + 8(i/4) + 4g + i%4.
-  if (qrow < Nq) {
-    float* dqr = p.dq + pv.qbase + (size_t)qrow * rs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 a;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = dq[db][4 * j + u] * p.scale;
-        *(f32x4*)(dqr + 32 * db + 8 * j + 4 * g) = a;
-      }
-  }
+  // dQ^T: lane column = query, element i = dim 32db + 8(i/4) + 4g + i%4. It goes out through
+  // LDS in whole row segments (store_rows_staged), once every wave has finished with the
+  // K/V stages.
+  wait_loads();
+  wg_barrier();
+  static_assert((kT / 64) * 32 * 64 * 4 <= (int)sizeof(smem), "epilogue staging exceeds the LDS");
+  store_rows_staged<D>(dq, p.scale, smem + w * (32 * 64 * 4), p.dq + pv.qbase + (size_t)wq0 * rs, (size_t)rs,
+                       Nq - wq0, lane);
 }
 
 template <int D, bool BIAS = false>

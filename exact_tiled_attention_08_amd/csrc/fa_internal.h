@@ -216,6 +216,58 @@ int fwd_bf16_block_rows(int d);
 int fwd_bf16_key_tile(int d);  // keys per K/V tile of fa_fwd's bfloat16 kernel
 int fwd_f32_block_rows(int d);
 
+// Stores a wave's 32 x D float32 tile of MFMA accumulators (lane column = row, element i of
+// acc[db] = column 32db + 8(i/4) + 4g + i%4, g = lane / 32), each lane's values times `mul`,
+// to rows 0 .. nvalid-1 of `out` (row stride rs floats). A lane holds 16-byte pieces of
+// one row, so storing them directly writes 32 bytes of each of 32 rows per instruction.
+// Here they pass through the wave's own 8 KB of LDS at `stage`, 64 columns at a time,
+// and are read back row-major: each store then writes whole 256-byte segments of 4 rows.
+// Chunk c of row r sits at chunk position c ^ (r % 16), which keeps both the writes and
+// the reads free of bank conflicts. The stores are non-temporal (the outputs are written
+// once and not read by the kernel; streamed past L2 they leave its K/V tiles there).
+// The caller makes sure no other wave uses `stage` meanwhile. (The two prefill kernels keep
+// an inline copy of these steps: through this function their code came out with other
+// register assignments and measured 0.35-0.6% slower.)
+template <int D>
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float mul, char* stage,
+                                                  float* out, size_t rs, int nvalid, int lane) {
+  const int col = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int hh = 0; hh < D / 64; ++hh) {
+#pragma unroll
+    for (int dbh = 0; dbh < 2; ++dbh)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int db = 2 * hh + dbh;
+        f32x4 val;
+        val[0] = acc[db][4 * j + 0] * mul;
+        val[1] = acc[db][4 * j + 1] * mul;
+        val[2] = acc[db][4 * j + 2] * mul;
+        val[3] = acc[db][4 * j + 3] * mul;
+        const int c = 8 * dbh + 2 * j + g;  // columns 64 hh + 4c .. 64 hh + 4c + 3
+        *(f32x4*)(stage + col * 256 + ((c ^ (col & 15)) << 4)) = val;
+      }
+    asm volatile("" ::: "memory");  // one wave's LDS accesses complete in issue order
+    const int c = lane & 15;
+    f32x4 rd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      rd[i] = *(const f32x4*)(stage + r * 256 + ((c ^ (r & 15)) << 4));
+    }
+    float* const obase = out + (size_t)(lane >> 4) * rs + 64 * hh + 4 * c;
+    if (nvalid >= 32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(rd[i], (f32x4*)(obase + (size_t)(4 * i) * rs));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (4 * i + (lane >> 4) < nvalid) __builtin_nontemporal_store(rd[i], (f32x4*)(obase + (size_t)(4 * i) * rs));
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 // Key rows per dK/dV workgroup and query rows per dQ workgroup of the backward pass.
 constexpr int kBwdKeyRows = 128;
 constexpr int kBwdQueryRows = 128;
