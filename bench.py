@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+CPU_SECONDS = 12.0          # target length of each sampled oracle run (--cpu-seconds)
 METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak (prefill); HBM GB/s (decode)"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -178,17 +179,19 @@ def visible_keys(w, rows):
     return np.full(i.shape, w.Nk, dtype=np.int64)
 
 
-def cpu_baseline(w, q, k, v, target_s: float, full: bool = False):
+def cpu_baseline(w, q, k, v, target_s: float, full: bool = False, bias=None):
     """Time the float64 oracle, unmodified, on this host's cores over the same workload and
     report its algorithmic rate (the GPU figure's FLOP or byte convention).
 
     full: every query row of the workload. Otherwise a uniform random sample of rows sized
     for about target_s seconds (a 256-row probe sets the size), reported with the time the
-    whole workload would take at the sample's rate (time scales with the visible keys)."""
+    whole workload would take at the sample's rate (time scales with the visible keys).
+    bias: the leg's additive bias, handed to the oracle as it is (a host copy is made)."""
     import numpy as np
     import oracle
     t_copy = time.perf_counter()
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    bc = bias.cpu() if bias is not None else None
     copy_s = time.perf_counter() - t_copy
     threads = oracle.default_threads()
     total_rows = w.B * w.H * w.Nq
@@ -202,13 +205,13 @@ def cpu_baseline(w, q, k, v, target_s: float, full: bool = False):
     else:
         probe = np.sort(rng.choice(total_rows, size=min(total_rows, 256), replace=False))
         t0 = time.perf_counter()
-        oracle.attention(qc, kc, vc, w.scale, w.causal, rows=probe, threads=threads)
+        oracle.attention(qc, kc, vc, w.scale, w.causal, rows=probe, threads=threads, bias=bc)
         rate = row_flops(probe) / max(1e-6, time.perf_counter() - t0)
         per_row = row_flops(probe) / len(probe)
         n = int(min(total_rows, max(256, target_s * rate / per_row)))
         rows = np.sort(rng.choice(total_rows, size=n, replace=False))
     t0 = time.perf_counter()
-    oracle.attention(qc, kc, vc, w.scale, w.causal, rows=rows, threads=threads)
+    oracle.attention(qc, kc, vc, w.scale, w.causal, rows=rows, threads=threads, bias=bc)
     sec = time.perf_counter() - t0
     flops = row_flops(np.arange(total_rows) if rows is None else rows)
     rec = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -226,6 +229,31 @@ def cpu_baseline(w, q, k, v, target_s: float, full: bool = False):
     if w.num_splits:  # decode: the same figure in the GPU leg's unit
         rec["value_gbps"] = w.io_bytes / sec / 1e9
     return rec
+
+
+def cpu_baseline_part(run, part_flops: float, whole_flops: float, sample: str):
+    """Time run(), one call of the float64 oracle, unmodified, on a part of a leg's workload
+    that holds part_flops of the leg's algorithmic FLOPs (whole_flops for the whole), and
+    report the oracle's rate in that convention, with the whole workload's time at that rate
+    when the part is not the whole."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    run(threads)
+    sec = time.perf_counter() - t0
+    rec = {"value": part_flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "seconds": sec, "sample": f"{sample}; {part_flops / 1e9:.1f} GFLOP in {sec:.1f} s"}
+    if part_flops < whole_flops:
+        rec["extrapolated_full_workload_s"] = sec * whole_flops / part_flops
+        rec["extrapolation"] = "the part's time scaled by the whole workload's FLOPs over the part's"
+    return rec
+
+
+def head_slice(t, dim: int = 1):
+    """Head 0 (of batch entry 0 for [B, H, N, d] tensors) as a contiguous host copy."""
+    if dim == 1:
+        return t[:1, :1].contiguous().cpu()
+    return t[:, :1].contiguous().cpu()  # packed [total, H, d]
 
 
 def prefill_record(num: int, steps: int, warmup: int, warmup_s: float | None = None):
@@ -257,7 +285,7 @@ def prefill_record(num: int, steps: int, warmup: int, warmup_s: float | None = N
     return rec, (w, q, k, v)
 
 
-def bias_record(num: int, steps: int, warmup: int):
+def bias_record(num: int, steps: int, warmup: int, cpu: bool = False):
     """fa_fwd_bias on workload `num` with a full [B, H, Nq, Nk] bias of its dtype (seeded,
     N(0,1) x 2): the general additive bias, nothing broadcast."""
     import torch
@@ -289,12 +317,16 @@ def bias_record(num: int, steps: int, warmup: int):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for("fwd_bf16_bias", num)},
     }
+    if cpu:  # sampled rows with the same bias, extrapolated; also in the leg's unit
+        cb = cpu_baseline(w, q, k, v, CPU_SECONDS, bias=bias)
+        cb["value_gbps"] = nbytes / cb["extrapolated_full_workload_s"] / 1e9
+        rec["cpu_baseline"] = cb
     del q, k, v, bias, o, lse
     torch.cuda.empty_cache()
     return rec
 
 
-def fp8_record(num: int, steps: int, warmup: int):
+def fp8_record(num: int, steps: int, warmup: int, cpu: bool = False):
     """fa_fwd_fp8 on workload `num`'s shape with its draws quantised per tensor to E4M3."""
     import torch
     import exact_tiled_attention_08_amd as fa
@@ -318,12 +350,16 @@ def fp8_record(num: int, steps: int, warmup: int):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic_for("fwd_fp8", num)},
     }
+    if cpu:  # the oracle on the values the kernel multiplies (E4M3 x descale, exact in float64)
+        deq = [x.cpu().to(torch.float64) * dsc for x, dsc in ((q8, qd), (k8, kd), (v8, vd))]
+        rec["cpu_baseline"] = cpu_baseline(w, *deq, CPU_SECONDS)
+        del deq
     del q8, k8, v8, o, lse
     torch.cuda.empty_cache()
     return rec
 
 
-def varlen_record(steps: int, warmup: int):
+def varlen_record(steps: int, warmup: int, cpu: bool = False):
     """fa_fwd_varlen on the packed batch of 16 causal sequences of seeded lengths."""
     import torch
     import exact_tiled_attention_08_amd as fa
@@ -349,12 +385,18 @@ def varlen_record(steps: int, warmup: int):
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic_for("fwd_bf16_varlen", "varlen")},
     }
+    if cpu:  # head 0 of the packed batch: every sequence, 1/H of the work
+        import oracle
+        qh, kh, vh, cuh = head_slice(q, 0), head_slice(k, 0), head_slice(v, 0), cu.cpu()
+        rec["cpu_baseline"] = cpu_baseline_part(
+            lambda t: oracle.attention_varlen(qh, kh, vh, cuh, cuh, scale, True, threads=t),
+            W.varlen_flops(lens, H=1), flops, f"head 0 of {H}: all {len(lens)} sequences, every row")
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return rec
 
 
-def bwd_record(num: int, steps: int, warmup: int):
+def bwd_record(num: int, steps: int, warmup: int, cpu: bool = False):
     """fa_bwd over workload `num` with the seeded dO; o and lse from fa_fwd (not timed)."""
     import torch
     import exact_tiled_attention_08_amd as fa
@@ -386,12 +428,19 @@ def bwd_record(num: int, steps: int, warmup: int):
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": bwd_traffic(num)},
     }
+    if cpu:  # one (b, h) of B*H: all of its query and key rows
+        import oracle
+        sl = [head_slice(t) for t in (q, k, v, do)]
+        rec["cpu_baseline"] = cpu_baseline_part(
+            lambda t: oracle.attention_bwd(*sl, w.scale, w.causal, threads=t),
+            w.bwd_flops / (w.B * w.H), w.bwd_flops,
+            f"(b, h) = (0, 0) of {w.B * w.H}: dQ, dK, dV of every row")
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return rec
 
 
-def bwd_bias_record(num: int, steps: int, warmup: int):
+def bwd_bias_record(num: int, steps: int, warmup: int, cpu: bool = False):
     """fa_bwd_bias over workload `num` with its full [B, H, Nq, Nk] bias (as in the biased
     prefill leg) and the seeded dO; o and lse from fa_fwd_bias (not timed); no dBias."""
     import torch
@@ -425,12 +474,20 @@ def bwd_bias_record(num: int, steps: int, warmup: int):
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": bwd_traffic(f"bias{num}")},
     }
+    if cpu:  # one (b, h) of B*H with its bias: all of its query and key rows
+        import oracle
+        sl = [head_slice(t) for t in (q, k, v, do)]
+        bh = head_slice(bias)
+        rec["cpu_baseline"] = cpu_baseline_part(
+            lambda t: oracle.attention_bwd(*sl, w.scale, w.causal, threads=t, bias=bh),
+            w.bwd_flops / (w.B * w.H), w.bwd_flops,
+            f"(b, h) = (0, 0) of {w.B * w.H} with its bias: dQ, dK, dV of every row")
     del q, k, v, bias, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return rec
 
 
-def bwd_varlen_record(steps: int, warmup: int):
+def bwd_varlen_record(steps: int, warmup: int, cpu: bool = False):
     """fa_bwd_varlen on the packed batch of the variable-length prefill leg with a seeded dO;
     o and lse from fa_fwd_varlen (not timed)."""
     import torch
@@ -466,6 +523,14 @@ def bwd_varlen_record(steps: int, warmup: int):
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": bwd_traffic("varlen")},
     }
+    if cpu:  # head 0 of the packed batch: every sequence, 1/H of the work
+        import oracle
+        sl = [head_slice(t, 0) for t in (q, k, v, do)]
+        cuh = cu.cpu()
+        rec["cpu_baseline"] = cpu_baseline_part(
+            lambda t: oracle.attention_varlen_bwd(*sl, cuh, cuh, scale, True, threads=t),
+            2.5 * W.varlen_flops(lens, H=1), flops,
+            f"head 0 of {H}: dQ, dK, dV of all {len(lens)} sequences")
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return rec
@@ -504,7 +569,7 @@ def decode_record(steps: int, warmup: int, cpu: bool = False):
     return rec
 
 
-def paged_decode_record(steps: int, warmup: int, page_size: int = 64):
+def paged_decode_record(steps: int, warmup: int, page_size: int = 64, cpu: bool = False):
     """fa_decode_paged on the decode workload's cache laid out in pages placed in a seeded
     random order across the pool (same keys, same bytes, page-table addressing)."""
     import torch
@@ -538,6 +603,15 @@ def paged_decode_record(steps: int, warmup: int, page_size: int = 64):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_for("decode_paged", 5)},
     }
+    if cpu:  # every sequence through the oracle's own page gather
+        import oracle
+        hq, hk, hv, ht, hl = q.cpu(), kc.cpu(), vc.cpu(), table.cpu(), lens.cpu()
+        cb = cpu_baseline_part(
+            lambda t: oracle.paged_attention(hq, hk, hv, ht, hl, page_size, w.scale, threads=t),
+            w.flops, w.flops, f"full workload: all {w.B * w.H} (b, h) over the paged pool")
+        cb["value_gbps"] = nbytes / cb["seconds"] / 1e9
+        rec["cpu_baseline"] = cb
+        del hq, hk, hv
     del q, kc, vc
     torch.cuda.empty_cache()
     return rec
@@ -647,6 +721,8 @@ def main():
         "clock": clock,
     }
     cpu = args.only is None and not args.no_cpu
+    global CPU_SECONDS
+    CPU_SECONDS = args.cpu_seconds
     if cpu:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     del q, k, v
@@ -675,16 +751,21 @@ def main():
             extra[key] = rec
             del qx, kx, vx
         torch.cuda.empty_cache()
-        extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
-        extra["prefill_fp8_N30000"] = fp8_record(4, max(3, args.steps // 5), max(1, args.warmup // 5))
-        extra["prefill_bias"] = bias_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
-        extra["prefill_varlen"] = varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
+        extra["prefill_fp8"] = fp8_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2),
+                                          cpu=cpu)
+        extra["prefill_fp8_N30000"] = fp8_record(4, max(3, args.steps // 5), max(1, args.warmup // 5),
+                                                 cpu=cpu)
+        extra["prefill_bias"] = bias_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2),
+                                            cpu=cpu)
+        extra["prefill_varlen"] = varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2), cpu=cpu)
         extra["decode"] = decode_record(max(5, args.steps), max(2, args.warmup), cpu=cpu)
-        extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup))
-        extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2))
+        extra["decode_paged"] = paged_decode_record(max(5, args.steps), max(2, args.warmup), cpu=cpu)
+        extra["backward"] = bwd_record(args.workload, max(5, args.steps // 2), max(2, args.warmup // 2),
+                                       cpu=cpu)
         extra["backward_bias"] = bwd_bias_record(args.workload, max(5, args.steps // 2),
-                                                 max(2, args.warmup // 2))
-        extra["backward_varlen"] = bwd_varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2))
+                                                 max(2, args.warmup // 2), cpu=cpu)
+        extra["backward_varlen"] = bwd_varlen_record(max(5, args.steps // 2), max(2, args.warmup // 2),
+                                                     cpu=cpu)
         out["also"] = extra
     print(json.dumps(out), flush=True)
 
