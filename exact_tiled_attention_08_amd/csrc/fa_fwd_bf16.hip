@@ -99,15 +99,12 @@ __device__ __forceinline__ void poison16(char* lds_slot) {
 // push out of L2 the K/V tiles that the other query tiles of a head read again (measured:
 // 5% faster biased prefill, no change in results).
 __device__ __forceinline__ void dma16_once(const void* base, uint32_t off, uint32_t lds_base) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
       : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
+      : "memory", "m0");
 }
 
 template <int D, int BC>

@@ -163,17 +163,16 @@ __device__ __forceinline__ void wait_loads_but() {
 // buffers as possible readers of this copy and stall them on vmcnt; completion is awaited
 // explicitly with wait_loads() before the barrier that publishes the buffer. The offset
 // register is the caller's long-lived VGPR, so no later instruction overwrites it while
-// the load is in flight. M0 is saved and restored around the copy.
+// the load is in flight. M0 is declared clobbered, so the compiler keeps nothing of its own
+// there across the copy and no save and restore is needed (two fewer scalar instructions
+// per load in the loops' issue bursts; measured +0.2% on both causal prefill shapes).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(off), "s"(base), "s"(lds_base)
-      : "memory");
+      : "memory", "m0");
 }
 
 // dma16 to LDS byte address lds_base + IMM: the constant is added to M0 inside the copy, so
@@ -181,15 +180,12 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 // keep one scalar per slot alive across the loop and spill them to vector registers).
 template <int IMM>
 __device__ __forceinline__ void dma16_at(const void* base, uint32_t off, uint32_t lds_base) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_add_u32 m0, %3, %4\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_add_u32 m0, %2, %3\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(off), "s"(base), "s"(lds_base), "i"(IMM)
-      : "memory", "scc");
+      : "memory", "scc", "m0");
 }
 
 // Launchers (defined next to their kernels). Each returns the hipError_t of the launch.
