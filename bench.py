@@ -644,9 +644,9 @@ def main():
                          "1 GiB device copy, the reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path shards over (batch, head) with no exchange, "
-              "and runs on more than one GPU are not part of this build; use --gpus 1",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the path shards over (batch, head) with no "
+              "exchange between GPUs, so each GPU runs its own share as this one-GPU line "
+              "measures it; use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
